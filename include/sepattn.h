@@ -1,0 +1,219 @@
+/*
+ * sepattn.h — C ABI of the SepLLM separator-mask attention and SepCache
+ * library for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (the pages about SepLLM, arXiv 2412.12094):
+ *   [ANTH] anthology-of-the-sota record LIT-748, "Key takeaways": the mask
+ *          bullet (each query sees the first a tokens, every separator so
+ *          far and its n nearest tokens; the same mask in every head; the
+ *          nine separator characters) and the streaming bullet (a bounded
+ *          cache, 324 entries).
+ *   [PITH] pith.science verdict for 2412.12094, pith_extraction.key_machinery:
+ *          the binary mask M; the streaming cache of initial, separator and
+ *          window blocks, in which leaving separators move to the separator
+ *          cache and other leaving tokens are dropped.
+ *   [HUB]  paperhub.cn author responses, second reviewer, answer A1: RoPE at
+ *          positions counted inside the cache (position shifting), plain RoPE
+ *          for training-length inputs.
+ *
+ * Conventions for every call:
+ *   - Data pointers are device pointers owned by the caller (for example
+ *     PyTorch tensors).  The library never allocates or frees device memory.
+ *     Pointers documented as "host" are read before the call returns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; none waits for the device, except
+ *     sepcache_rope_table, which copies a host table and waits for the copy.
+ *   - The return value is a status code (SEPATTN_OK = 0 or a negative error).
+ *     Arguments are validated before any launch; on error nothing is
+ *     enqueued and sepattn_last_error() gives a description (per thread).
+ *   - Floating-point tensors are bf16 (SEPATTN_BF16) or fp32 (SEPATTN_F32);
+ *     accumulation is fp32.  Head dimension d is 64 or 128.
+ *   - Indices are 0-based.  a = number of sinks (initial tokens), n = window
+ *     size, which counts the query itself: row i keeps j in (i-n, i].
+ */
+#ifndef SEPATTN_H
+#define SEPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef SEPATTN_API
+#define SEPATTN_API __attribute__((visibility("default")))
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SEPATTN_OK = 0,
+  SEPATTN_EINVAL = -1,  /* bad argument (shape, size, null pointer, range) */
+  SEPATTN_ENOTSUP = -2, /* valid but unsupported (head dim, dtype, device)  */
+  SEPATTN_EHIP = -3,    /* a HIP runtime call failed                        */
+  SEPATTN_ESPACE = -4   /* caller-provided buffer or workspace too small    */
+};
+
+enum { SEPATTN_F32 = 0, SEPATTN_BF16 = 1 };
+
+#define SEPATTN_MAX_SEP_IDS 64
+
+/* Text of the last error returned on this thread ("" if none). */
+SEPATTN_API const char* sepattn_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+SEPATTN_API int sepattn_version(void);
+
+/* ------------------------------------------------------------------------
+ * Mask metadata ([ANTH] mask bullet; [PITH] key_machinery (i)-(iii)).
+ *
+ * M[b,i,j] = (j <= i) and (j < a  or  i - j < n  or  f[b,j] = 1), where
+ * f[b,j] = 1 iff token j of sequence b is a separator.  Nothing dense is
+ * stored: the kernels work from the compacted lists below.
+ *
+ * "Anchors" are the keys every later row sees: sinks j < a and separators.
+ * A sink whose token is a separator is a sink only (never in sep_idx).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int B, L;            /* sequences, tokens per sequence                        */
+  int a, n;            /* sinks (a >= 0), window (n >= 1, counts the query)      */
+  uint8_t* is_sep;     /* [B, L]   f[b, j]                                      */
+  int32_t* sep_idx;    /* [B, L]   ascending separator positions j >= a; the
+                                   tail after sep_cnt[b] entries is set to L     */
+  int32_t* sep_before; /* [B, L+1] number of separators (j >= a) before position */
+  int32_t* sep_cnt;    /* [B]      separators at positions >= a                 */
+  int32_t* plain_idx;  /* [B, L]   ascending positions j >= a with f = 0; tail L */
+  int32_t* plain_cnt;  /* [B]                                                   */
+  int64_t* kept;       /* [B]      number of (i, j) with M = 1                   */
+} sepattn_mask;
+
+/* Bytes of one device buffer that sepattn_mask_carve() splits into the
+ * arrays of a mask for B sequences of L tokens (256-byte aligned pieces). */
+SEPATTN_API size_t sepattn_mask_bytes(int B, int L);
+/* Fill m's pointers from one caller-owned device buffer of at least
+ * sepattn_mask_bytes(B, L) bytes and set B, L, a, n.  No device work. */
+SEPATTN_API int sepattn_mask_carve(sepattn_mask* m, int B, int L, int a, int n, void* buffer, size_t bytes);
+
+/* Build the mask metadata from token ids.
+ *   tok     device int32 [B, L], contiguous.
+ *   sep_ids host int32 [n_sep], 1 <= n_sep <= SEPATTN_MAX_SEP_IDS: the token ids
+ *           of the separators (the pages' nine characters, as token ids).
+ *   m       metadata with B, L, a, n and all pointers set.
+ * One launch; fills every array of m. */
+SEPATTN_API int sepattn_build_mask(const int32_t* tok, const int32_t* sep_ids, int n_sep,
+                       const sepattn_mask* m, void* stream);
+
+/* Expand the metadata into the dense mask, bit-packed: bits[b][i][w] holds
+ * M[b,i,32w+t] in bit t, for w < ceil(L/32); bits past L are 0.  The kernel
+ * walks each row the way the forward kernel does (gathered anchors, then the
+ * band with its element test), so this checks the forward's traversal.
+ * bits: device uint32 [B, L, ceil(L/32)].  For testing; L <= 65536. */
+SEPATTN_API int sepattn_mask_bits(const sepattn_mask* m, uint32_t* bits, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Attention under M (prefill / training; [ANTH] mask bullet: the mask is
+ * trained through, forward and backward).
+ *
+ * Q, O, dO, dQ: [B, Hq, L, d]; K, V, dK, dV: [B, Hkv, L, d], addressed with
+ * element strides (batch, head, token) and a contiguous last dimension.
+ * q head h reads KV head h / (Hq / Hkv).  Inputs already carry their
+ * positional encoding (plain RoPE for training-length inputs, [HUB] A1).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int B, Hq, Hkv, L, d;
+  int64_t q_stride[3]; /* also used for dQ */
+  int64_t k_stride[3]; /* also used for dK */
+  int64_t v_stride[3]; /* also used for dV */
+  int64_t o_stride[3]; /* also used for dO */
+} sepattn_shape;
+
+/* O = softmax(scale * Q K^T restricted to M) V; lse[b,h,i] = natural
+ * log-sum-exp of row i's kept scaled scores.  dtype applies to q, k, v, o.
+ * lse: device fp32 [B, Hq, L] contiguous, or NULL.  m must come from
+ * sepattn_build_mask for the same B, L.  Every row keeps key j = i, so no row
+ * is empty. */
+SEPATTN_API int sepattn_fwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
+                const void* q, const void* k, const void* v, float scale,
+                void* o, float* lse, void* stream);
+
+/* Workspace bytes for sepattn_bwd (fp32 D = rowsum(dO * O), [B, Hq, L]). */
+SEPATTN_API size_t sepattn_bwd_workspace_size(const sepattn_shape* s);
+
+/* Gradients for upstream dO: with P the masked softmax,
+ *   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q,
+ * dK/dV summed over the q heads of each KV head.  o and lse are the forward's
+ * outputs; dout uses o's strides; dq, dk, dv are written (not accumulated).
+ * Deterministic: no atomics; every output row is written by one workgroup. */
+SEPATTN_API int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
+                const void* q, const void* k, const void* v, const void* o,
+                const float* lse, const void* dout, float scale,
+                void* dq, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * SepCache: the streaming cache ([PITH] key_machinery; [ANTH] streaming
+ * bullet) with a sink block of a entries, a separator block of s entries kept
+ * first-in first-out, and a window of n entries (the newest token included).
+ * Per step: append the new token, evict (a token leaving the window moves to
+ * the separator block if it is a separator, dropping that block's oldest
+ * entry when full, and is dropped otherwise), then decode.  After eviction
+ * the cache holds at most a + s + n entries.  The cache's logical order is
+ * sinks, separators (oldest first), window (oldest first), which is
+ * ascending original position.
+ *
+ * All streams of a batch share the step: stream b appends its own token and
+ * flag.  Physical slots per stream: [0, a) sinks, [a, a+s) separator ring,
+ * [a+s, a+s+n+1) window ring (one spare slot for the appended token).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int B, Hkv, d;       /* streams, KV heads, head dim (64 or 128)              */
+  int a, s, n;         /* sinks, separator capacity (>= 0), window (>= 1)       */
+  void* k;             /* bf16 [B, Hkv, slots, d] keys before RoPE              */
+  void* v;             /* bf16 [B, Hkv, slots, d]                               */
+  int32_t* slot_pos;   /* [B, slots] original position held, -1 if empty        */
+  uint8_t* slot_sep;   /* [B, slots] separator flag of the token held           */
+  int32_t* state;      /* [B, 8] counters: tokens seen, sinks, sep head, sep
+                          count, window head, window count, 2 reserved          */
+  const float* rope;   /* fp32 [rope_len, d/2, 2] (cos, sin) from
+                          sepcache_rope_table                                   */
+  int rope_len;        /* positions covered by the table                        */
+} sepcache;
+
+/* Physical slots per stream and KV head: a + s + n + 1. */
+SEPATTN_API int sepcache_slots(int a, int s, int n);
+/* Fill a device fp32 table [len, d/2, 2] with cos and sin of p * w_i,
+ * w_i = theta^(-2i/d) (half-split RoPE pairing dimension i with i + d/2),
+ * computed in double precision on the host.  Position shifting needs
+ * len >= a + s + n; original positions need len > the largest position.
+ * Copies synchronously. */
+SEPATTN_API int sepcache_rope_table(float* table, int len, int d, float theta, void* stream);
+/* Empty every stream (slot_pos = -1, counters 0). */
+SEPATTN_API int sepcache_reset(const sepcache* c, void* stream);
+/* Append token t of every stream: k_new, v_new bf16 [B, Hkv, d] contiguous,
+ * is_sep device uint8 [B].  Token t < a becomes a sink, later tokens enter the
+ * window.  Call sepcache_evict before the next append. */
+SEPATTN_API int sepcache_append(const sepcache* c, const void* k_new, const void* v_new,
+                    const uint8_t* is_sep, void* stream);
+/* If a stream's window holds more than n entries, its oldest entry leaves:
+ * to the separator block (separator) or dropped (other). */
+SEPATTN_API int sepcache_evict(const sepcache* c, void* stream);
+/* append + evict in one launch. */
+SEPATTN_API int sepcache_push(const sepcache* c, const void* k_new, const void* v_new,
+                  const uint8_t* is_sep, void* stream);
+/* Attention of the newest token over the cache: for q head h (KV head
+ * h / (Hq / Hkv)), keys rotated by RoPE at their positions, the query at its
+ * own, softmax(scale * q.k) over every entry, times V.  shift != 0: positions
+ * are ranks in the logical order (the query is the last rank, [HUB] A1);
+ * shift == 0: original token positions.
+ *   q bf16 [B, Hq, d] (before RoPE), o bf16 [B, Hq, d], contiguous.
+ *   workspace: sepcache_decode_workspace_size() bytes of device memory. */
+SEPATTN_API size_t sepcache_decode_workspace_size(const sepcache* c, int Hq);
+SEPATTN_API int sepcache_decode(const sepcache* c, int Hq, const void* q, float scale, int shift,
+                    void* o, void* workspace, size_t workspace_bytes, void* stream);
+/* Original positions in logical order: pos [B, a+s+n] (unused tail -1),
+ * len [B] entries held.  For bit-exact checks against a reference. */
+SEPATTN_API int sepcache_export_order(const sepcache* c, int32_t* pos, int32_t* len, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SEPATTN_H */

@@ -1,0 +1,206 @@
+"""Thin torch-facing binding of the C ABI: argument marshalling only.
+
+Tensors are PyTorch device tensors; work is enqueued on torch's current
+stream.  Every computation happens in the HIP kernels of libsepattn.so; if
+the library is missing, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import BF16, F32, SepattnMask, SepattnShape, SepCacheStruct, check
+
+_DT = {torch.bfloat16: BF16, torch.float32: F32}
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+class Mask:
+    """Mask metadata for B sequences of L tokens in one device buffer."""
+
+    def __init__(self, B: int, L: int, a: int, n: int, device="cuda"):
+        lib = _lib.load()
+        nbytes = lib.sepattn_mask_bytes(B, L)
+        if nbytes == 0:
+            raise ValueError(f"bad mask size B={B} L={L}")
+        self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.c = SepattnMask()
+        check(lib.sepattn_mask_carve(ctypes.byref(self.c), B, L, a, n, _ptr(self.buffer), nbytes))
+        self.B, self.L, self.a, self.n = B, L, a, n
+
+    def _view(self, field: str, dtype, shape):
+        off = getattr(self.c, field) - self.buffer.data_ptr()
+        count = math.prod(shape)
+        nbytes = count * torch.empty((), dtype=dtype).element_size()
+        return self.buffer[off:off + nbytes].view(dtype).view(shape)
+
+    @property
+    def is_sep(self): return self._view("is_sep", torch.uint8, (self.B, self.L))
+    @property
+    def sep_idx(self): return self._view("sep_idx", torch.int32, (self.B, self.L))
+    @property
+    def sep_before(self): return self._view("sep_before", torch.int32, (self.B, self.L + 1))
+    @property
+    def sep_cnt(self): return self._view("sep_cnt", torch.int32, (self.B,))
+    @property
+    def plain_idx(self): return self._view("plain_idx", torch.int32, (self.B, self.L))
+    @property
+    def plain_cnt(self): return self._view("plain_cnt", torch.int32, (self.B,))
+    @property
+    def kept(self): return self._view("kept", torch.int64, (self.B,))
+
+
+def build_mask(tok: torch.Tensor, sep_ids, a: int, n: int) -> Mask:
+    """sepattn_build_mask: tok int32 [B, L] on the device."""
+    if tok.dtype != torch.int32 or tok.dim() != 2 or not tok.is_contiguous():
+        raise ValueError("tok must be a contiguous int32 [B, L] tensor")
+    B, L = tok.shape
+    m = Mask(B, L, a, n, tok.device)
+    ids = (ctypes.c_int32 * len(sep_ids))(*[int(x) for x in sep_ids])
+    check(_lib.load().sepattn_build_mask(_ptr(tok), ids, len(sep_ids), ctypes.byref(m.c), _stream()))
+    return m
+
+
+def mask_bits(m: Mask) -> torch.Tensor:
+    """sepattn_mask_bits: the dense mask as uint32 words [B, L, ceil(L/32)]
+    (int32 storage holding the same bits)."""
+    words = (m.L + 31) // 32
+    bits = torch.empty((m.B, m.L, words), dtype=torch.int32, device=m.buffer.device)
+    check(_lib.load().sepattn_mask_bits(ctypes.byref(m.c), _ptr(bits), _stream()))
+    return bits
+
+
+def _shape(q, k, v, o) -> SepattnShape:
+    for t in (q, k, v, o):
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError("attention tensors must be 4-d [B, H, L, d] with a contiguous last dimension")
+    s = SepattnShape()
+    s.B, s.Hq, s.L, s.d = q.shape
+    s.Hkv = k.shape[1]
+    if k.shape != (s.B, s.Hkv, s.L, s.d) or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError(f"shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)} o{tuple(o.shape)}")
+    for name, t in (("q_stride", q), ("k_stride", k), ("v_stride", v), ("o_stride", o)):
+        arr = getattr(s, name)
+        for i in range(3):
+            arr[i] = t.stride(i)
+    return s
+
+
+def sepattn_fwd(q, k, v, m: Mask, scale: float | None = None, out: torch.Tensor | None = None,
+                lse: torch.Tensor | None = None, want_lse: bool = True):
+    """sepattn_fwd: returns (O, LSE) with O like q and LSE fp32 [B, Hq, L]."""
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share dtype bf16 or fp32")
+    o = torch.empty_like(q) if out is None else out
+    B, Hq, L, d = q.shape
+    if want_lse and lse is None:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    s = _shape(q, k, v, o)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    check(_lib.load().sepattn_fwd(ctypes.byref(s), _DT[q.dtype], ctypes.byref(m.c), _ptr(q), _ptr(k), _ptr(v),
+                                  sc, _ptr(o), _ptr(lse if want_lse else None), _stream()))
+    return o, lse
+
+
+def sepattn_bwd(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, workspace=None):
+    """sepattn_bwd: returns (dQ, dK, dV)."""
+    if dout.stride() != o.stride():
+        raise ValueError("dout must have o's strides")
+    s = _shape(q, k, v, o)
+    lib = _lib.load()
+    need = lib.sepattn_bwd_workspace_size(ctypes.byref(s))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+    sc = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
+    check(lib.sepattn_bwd(ctypes.byref(s), _DT[q.dtype], ctypes.byref(m.c), _ptr(q), _ptr(k), _ptr(v),
+                          _ptr(o), _ptr(lse), _ptr(dout), sc, _ptr(dq), _ptr(dk), _ptr(dv),
+                          _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return dq, dk, dv
+
+
+class SepCache:
+    """A SepCache for B streams (bf16 K/V) plus its RoPE table."""
+
+    def __init__(self, B: int, Hkv: int, d: int, a: int, s: int, n: int, theta: float = 500000.0,
+                 rope_len: int | None = None, device="cuda"):
+        lib = _lib.load()
+        slots = lib.sepcache_slots(a, s, n)
+        if slots < 0:
+            raise ValueError(f"bad cache sizes a={a} s={s} n={n}")
+        self.B, self.Hkv, self.d, self.a, self.s, self.n, self.slots = B, Hkv, d, a, s, n, slots
+        self.k = torch.zeros((B, Hkv, slots, d), dtype=torch.bfloat16, device=device)
+        self.v = torch.zeros((B, Hkv, slots, d), dtype=torch.bfloat16, device=device)
+        self.slot_pos = torch.empty((B, slots), dtype=torch.int32, device=device)
+        self.slot_sep = torch.empty((B, slots), dtype=torch.uint8, device=device)
+        self.state = torch.empty((B, 8), dtype=torch.int32, device=device)
+        self.rope_len = a + s + n if rope_len is None else rope_len
+        self.rope = torch.empty((self.rope_len, d // 2, 2), dtype=torch.float32, device=device)
+        check(lib.sepcache_rope_table(_ptr(self.rope), self.rope_len, d, float(theta), _stream()))
+        c = SepCacheStruct()
+        c.B, c.Hkv, c.d, c.a, c.s, c.n = B, Hkv, d, a, s, n
+        c.k, c.v = self.k.data_ptr(), self.v.data_ptr()
+        c.slot_pos, c.slot_sep, c.state = (self.slot_pos.data_ptr(), self.slot_sep.data_ptr(),
+                                           self.state.data_ptr())
+        c.rope, c.rope_len = self.rope.data_ptr(), self.rope_len
+        self.c = c
+        self._ws = None
+        self.reset()
+
+    def reset(self):
+        check(_lib.load().sepcache_reset(ctypes.byref(self.c), _stream()))
+
+    def _kvf(self, k_new, v_new, is_sep):
+        for t in (k_new, v_new):
+            if t.dtype != torch.bfloat16 or t.shape != (self.B, self.Hkv, self.d) or not t.is_contiguous():
+                raise ValueError("k_new/v_new must be contiguous bf16 [B, Hkv, d]")
+        if is_sep.dtype != torch.uint8 or is_sep.shape != (self.B,):
+            raise ValueError("is_sep must be uint8 [B]")
+
+    def append(self, k_new, v_new, is_sep):
+        self._kvf(k_new, v_new, is_sep)
+        check(_lib.load().sepcache_append(ctypes.byref(self.c), _ptr(k_new), _ptr(v_new), _ptr(is_sep), _stream()))
+
+    def evict(self):
+        check(_lib.load().sepcache_evict(ctypes.byref(self.c), _stream()))
+
+    def push(self, k_new, v_new, is_sep):
+        self._kvf(k_new, v_new, is_sep)
+        check(_lib.load().sepcache_push(ctypes.byref(self.c), _ptr(k_new), _ptr(v_new), _ptr(is_sep), _stream()))
+
+    def workspace(self, Hq: int) -> torch.Tensor:
+        need = _lib.load().sepcache_decode_workspace_size(ctypes.byref(self.c), Hq)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=self.k.device)
+        return self._ws
+
+    def decode(self, q, scale: float | None = None, shift: bool = True, out=None):
+        """sepcache_decode: q bf16 [B, Hq, d] -> o bf16 [B, Hq, d]."""
+        if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[0] != self.B or not q.is_contiguous():
+            raise ValueError("q must be contiguous bf16 [B, Hq, d]")
+        Hq = q.shape[1]
+        o = torch.empty_like(q) if out is None else out
+        ws = self.workspace(Hq)
+        sc = 1.0 / math.sqrt(self.d) if scale is None else float(scale)
+        check(_lib.load().sepcache_decode(ctypes.byref(self.c), Hq, _ptr(q), sc, 1 if shift else 0, _ptr(o),
+                                          _ptr(ws), ws.numel(), _stream()))
+        return o
+
+    def export_order(self):
+        """sepcache_export_order: (pos int32 [B, a+s+n], len int32 [B])."""
+        pos = torch.empty((self.B, self.a + self.s + self.n), dtype=torch.int32, device=self.k.device)
+        ln = torch.empty((self.B,), dtype=torch.int32, device=self.k.device)
+        check(_lib.load().sepcache_export_order(ctypes.byref(self.c), _ptr(pos), _ptr(ln), _stream()))
+        return pos, ln

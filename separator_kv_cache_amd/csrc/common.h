@@ -1,0 +1,67 @@
+// Shared device/host helpers of the sepattn library (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sepattn.h"
+
+// ---------------------------------------------------------------- host side
+
+// Records an error text for sepattn_last_error() and returns `code`.
+int sepattn_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Checks a HIP call made while enqueueing work.
+int sepattn_hip_check(hipError_t e, const char* what);
+// Returns SEPATTN_OK if the current device is gfx950, else an error.
+int sepattn_check_device();
+
+#define SEPATTN_TRY(x)          \
+  do {                          \
+    int _rc = (x);              \
+    if (_rc != SEPATTN_OK) return _rc; \
+  } while (0)
+
+// ---------------------------------------------------------------- device side
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// D(32x32) += A(32x16) B(16x32), bf16 inputs, fp32 accumulate.
+// Lane l supplies A[l%32][8*(l/32) + 0..7] and B[8*(l/32) + 0..7][l%32];
+// result register r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// D(32x32) += A(32x2) B(2x32), fp32.  Lane l supplies A[l%32][l/32] and
+// B[l/32][l%32]; same result layout as above.
+__device__ __forceinline__ f32x16 mfma32x2f(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// LDS transposing read of 16-bit elements.  Within each group of 16 lanes,
+// lane i receives, for s = 0..3, element (i % 4) of the 4-element chunk
+// addressed by lane 4*s + i/4 of the same group.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+
+// 16-byte global loads and stores.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
+
+// Swap values between lane l and lane l ^ 32.
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -1,0 +1,45 @@
+// Key traversal of one query tile under the SepLLM mask.
+//
+// The mask (anthology record LIT-748, "Key takeaways", mask bullet; pith.science
+// key_machinery (i)-(iii)) keeps, for query i, key j <= i when j < a (sink),
+// i - j < n (window, the query included) or token j is a separator.
+//
+// For a tile of rows [q0, q0 + rows) let band_lo = max(0, q0 - n + 1).  A key
+// j < band_lo is outside the window of every row of the tile, so the tile sees
+// it iff it is a sink or a separator, and then every row sees it.  Those keys
+// are a prefix of one ascending list: sinks 0..min(a, band_lo)-1 followed by
+// the separators sep_idx[0 .. sep_before[band_lo]).  Keys in [band_lo,
+// band_hi) form the band, where the element test decides.
+#pragma once
+
+#include "common.h"
+
+struct TileKeys {
+  int band_lo, band_hi;  // band [band_lo, band_hi)
+  int n_sink;            // gathered sinks: keys 0 .. n_sink-1
+  int n_gather;          // gathered keys: n_sink sinks then separators
+};
+
+__device__ __forceinline__ TileKeys tile_keys(int q0, int rows, int L, int a, int n,
+                                              const int32_t* __restrict__ sep_before_b) {
+  TileKeys t;
+  t.band_lo = max(0, q0 - n + 1);
+  t.band_hi = min(L, q0 + rows);
+  t.n_sink = min(a, t.band_lo);
+  t.n_gather = t.n_sink + sep_before_b[t.band_lo];
+  return t;
+}
+
+// Key position of gathered entry c (c < n_gather).
+__device__ __forceinline__ int gather_key(int c, int n_sink, const int32_t* __restrict__ sep_idx_b) {
+  return c < n_sink ? c : sep_idx_b[c - n_sink];
+}
+
+// Element test of the band.
+__device__ __forceinline__ bool band_keep(int i, int j, int a, int n, const uint8_t* __restrict__ is_sep_b) {
+  return j <= i && (j < a || i - j < n || is_sep_b[j] != 0);
+}
+
+// Rows per query tile of the forward (and of the dQ pass), chosen from the
+// window only so that the mask expansion can reproduce the same tiling.
+static inline int fwd_tile_rows(int n) { return n <= 256 ? 64 : 128; }

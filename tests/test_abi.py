@@ -1,0 +1,109 @@
+"""The C ABI library loads, exports every declared entry point, and rejects
+bad arguments with status codes (validation precedes any HIP call, so these
+run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from separator_kv_cache_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "sepattn.h")).read()
+    return sorted(set(re.findall(r"SEPATTN_API\s+[\w\s\*]+?\b((?:sepattn|sepcache)_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for want in ("sepattn_build_mask", "sepattn_fwd", "sepattn_bwd", "sepcache_append", "sepcache_evict",
+                 "sepcache_decode"):
+        assert want in names
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.sepattn_version() >= 10000
+
+
+def _shape(B=1, Hq=4, Hkv=2, L=64, d=64):
+    s = _lib.SepattnShape()
+    s.B, s.Hq, s.Hkv, s.L, s.d = B, Hq, Hkv, L, d
+    for f in ("q_stride", "k_stride", "v_stride", "o_stride"):
+        arr = getattr(s, f)
+        H = Hq if f in ("q_stride", "o_stride") else Hkv
+        arr[0], arr[1], arr[2] = H * L * d, L * d, d
+    return s
+
+
+def _mask(B=1, L=64, a=4, n=8):
+    m = _lib.SepattnMask()
+    buf = ctypes.create_string_buffer(_lib.load().sepattn_mask_bytes(B, L) + 256)
+    base = (ctypes.addressof(buf) + 255) & ~255
+    rc = _lib.load().sepattn_mask_carve(ctypes.byref(m), B, L, a, n, ctypes.c_void_p(base),
+                                        _lib.load().sepattn_mask_bytes(B, L))
+    assert rc == _lib.OK
+    return m, buf
+
+
+def test_argument_validation_without_gpu():
+    lib = _lib.load()
+    m, _keep = _mask()
+    assert lib.sepattn_mask_bytes(0, 10) == 0
+    m2 = _lib.SepattnMask()
+    assert lib.sepattn_mask_carve(ctypes.byref(m2), 0, 5, 1, 1, ctypes.c_void_p(256), 10) == _lib.EINVAL
+    assert lib.sepattn_mask_carve(ctypes.byref(m2), 1, 5, 1, 0, ctypes.c_void_p(256), 10 ** 6) == _lib.EINVAL
+    assert lib.sepattn_mask_carve(ctypes.byref(m2), 1, 5, -1, 3, ctypes.c_void_p(256), 10 ** 6) == _lib.EINVAL
+    assert lib.sepattn_mask_carve(ctypes.byref(m2), 2, 100, 1, 3, ctypes.c_void_p(256), 64) == _lib.ESPACE
+    assert b"bytes" in lib.sepattn_last_error()
+    ids = (ctypes.c_int32 * 1)(5)
+    assert lib.sepattn_build_mask(None, ids, 1, ctypes.byref(m), None) == _lib.EINVAL
+    assert lib.sepattn_build_mask(ctypes.c_void_p(256), ids, 0, ctypes.byref(m), None) == _lib.EINVAL
+    assert lib.sepattn_build_mask(ctypes.c_void_p(256), ids, 65, ctypes.byref(m), None) == _lib.EINVAL
+    p = ctypes.c_void_p(4096)
+    s = _shape(Hq=3, Hkv=2)
+    assert lib.sepattn_fwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, 0.1, p, None, None) == _lib.EINVAL
+    assert b"multiple" in lib.sepattn_last_error()
+    s = _shape(d=96)
+    assert lib.sepattn_fwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, 0.1, p, None, None) == _lib.ENOTSUP
+    s = _shape()
+    assert lib.sepattn_fwd(ctypes.byref(s), 7, ctypes.byref(m), p, p, p, 0.1, p, None, None) == _lib.ENOTSUP
+    assert lib.sepattn_fwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), None, p, p, 0.1, p, None, None) == _lib.EINVAL
+    assert lib.sepattn_fwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), ctypes.c_void_p(4098), p, p, 0.1, p,
+                           None, None) == _lib.EINVAL
+    assert lib.sepattn_fwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, float("nan"), p, None,
+                           None) == _lib.EINVAL
+    s = _shape(L=65)
+    assert lib.sepattn_fwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, 0.1, p, None, None) == _lib.EINVAL
+    s = _shape()
+    s.q_stride[2] = 3
+    assert lib.sepattn_fwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, 0.1, p, None, None) == _lib.EINVAL
+    s = _shape()
+    need = lib.sepattn_bwd_workspace_size(ctypes.byref(s))
+    assert need >= 1 * 4 * 64 * 4
+    assert lib.sepattn_bwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, p, p, p, 0.1, p, p, p, p,
+                           need - 1, None) == _lib.ESPACE
+    assert lib.sepcache_slots(4, 64, 256) == 325
+    assert lib.sepcache_slots(4, 64, 0) == -1
+    c = _lib.SepCacheStruct()
+    c.B, c.Hkv, c.d, c.a, c.s, c.n = 2, 2, 64, 4, 8, 0
+    assert lib.sepcache_reset(ctypes.byref(c), None) == _lib.EINVAL
+    c.n, c.d = 16, 80
+    assert lib.sepcache_reset(ctypes.byref(c), None) == _lib.ENOTSUP
+    c.d = 64
+    assert lib.sepcache_reset(ctypes.byref(c), None) == _lib.EINVAL  # null arrays
+    c.k = c.v = c.slot_pos = c.slot_sep = c.state = 4096
+    assert lib.sepcache_decode(ctypes.byref(c), 3, p, 0.1, 1, p, p, 10 ** 6, None) == _lib.EINVAL  # no rope
+    c.rope, c.rope_len = 4096, 100
+    assert lib.sepcache_decode(ctypes.byref(c), 3, p, 0.1, 1, p, p, 10 ** 6, None) == _lib.EINVAL
+    assert lib.sepcache_decode(ctypes.byref(c), 32, p, 0.1, 1, p, p, 10 ** 6, None) == _lib.ENOTSUP
+    c.rope_len = 10
+    assert lib.sepcache_decode(ctypes.byref(c), 4, p, 0.1, 1, p, p, 10 ** 6, None) == _lib.EINVAL
+    assert lib.sepcache_rope_table(None, 10, 64, 10000.0, None) == _lib.EINVAL
+    assert lib.sepcache_rope_table(p, 10, 64, 0.5, None) == _lib.EINVAL
