@@ -205,7 +205,12 @@ SEPATTN_API int sepcache_push(const sepcache* c, const void* k_new, const void* 
  * are ranks in the logical order (the query is the last rank, [HUB] A1);
  * shift == 0: original token positions.
  *   q bf16 [B, Hq, d] (before RoPE), o bf16 [B, Hq, d], contiguous.
- *   workspace: sepcache_decode_workspace_size() bytes of device memory. */
+ *   workspace: sepcache_decode_workspace_size() bytes of device memory,
+ *   zero-filled by the caller before its first use; each call leaves its
+ *   counters at zero again.  Calls that share a workspace must not overlap.
+ * A query or key position outside the RoPE table (possible only without
+ * shifting, when the table is shorter than the stream) makes that output NaN.
+ * Decode before any append writes zeros. */
 SEPATTN_API size_t sepcache_decode_workspace_size(const sepcache* c, int Hq);
 SEPATTN_API int sepcache_decode(const sepcache* c, int Hq, const void* q, float scale, int shift,
                     void* o, void* workspace, size_t workspace_bytes, void* stream);

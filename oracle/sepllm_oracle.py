@@ -224,6 +224,29 @@ def attn_bwd(q, k, v, do, f, a: int, n: int, scale: float, block: int = 256, hea
     return dq, dk, dv
 
 
+def attn_bwd_rows(q, k, v, do, f, a: int, n: int, scale: float, b: int, h: int, rows):
+    """dQ for selected rows of one (sequence, q head), each row computed alone:
+    P_i over the row's kept keys, O_i = P_i V, D_i = dO_i . O_i,
+    dS_i = P_i (dO_i V^T - D_i), dQ_i = scale dS_i K."""
+    Hq, Hkv = q.shape[1], k.shape[1]
+    kh = h // (Hq // Hkv)
+    rows = np.asarray(rows)
+    out = np.zeros((len(rows), q.shape[-1]))
+    for t, i in enumerate(rows):
+        m = mask_rows(f[b], a, n, int(i), int(i) + 1, int(i) + 1)[0]
+        cols = np.nonzero(m)[0]
+        kc = k[b, kh, cols].astype(np.float64)
+        vc = v[b, kh, cols].astype(np.float64)
+        s = scale * (kc @ q[b, h, i].astype(np.float64))
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        dob = do[b, h, i].astype(np.float64)
+        D = dob @ (p @ vc)
+        ds = p * (vc @ dob - D)
+        out[t] = scale * (ds @ kc)
+    return out
+
+
 # --------------------------------------------------------------------------
 # RoPE and the streaming SepCache
 # --------------------------------------------------------------------------

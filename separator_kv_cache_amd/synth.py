@@ -164,13 +164,20 @@ class DecodeWorkload:
         """Separator indicator per (step, stream): uint8 [T, B], i.i.d. Bernoulli(p)."""
         return bernoulli(seed, self.wid, T_DEC_F, (self.T, self.B), self.p)
 
-    def step_inputs(self, seed: int = 0, steps: int | None = None):
-        """fp32 q [T,B,Hq,d], k/v [T,B,Hkv,d] drawn N(0,1)."""
-        T = self.T if steps is None else steps
-        q = gaussian(seed, self.wid, T_DEC_Q, (T, self.B, self.Hq, self.d))
-        k = gaussian(seed, self.wid, T_DEC_K, (T, self.B, self.Hkv, self.d))
-        v = gaussian(seed, self.wid, T_DEC_V, (T, self.B, self.Hkv, self.d))
-        return q, k, v
+    def _step(self, seed: int, tid: int, t: int, shape) -> np.ndarray:
+        rng = np.random.default_rng(np.random.SeedSequence(seed, spawn_key=(self.wid, tid, t)))
+        return rng.standard_normal(size=shape, dtype=np.float32)
+
+    def q_steps(self, steps, seed: int = 0) -> np.ndarray:
+        """fp32 queries N(0,1) of the given steps: [len(steps), B, Hq, d].
+        Each step has its own stream, so any subset is reproducible."""
+        return np.stack([self._step(seed, T_DEC_Q, int(t), (self.B, self.Hq, self.d)) for t in steps])
+
+    def kv_steps(self, t0: int, t1: int, seed: int = 0):
+        """fp32 new keys and values N(0,1) of steps [t0, t1): [t1-t0, B, Hkv, d] each."""
+        k = np.stack([self._step(seed, T_DEC_K, t, (self.B, self.Hkv, self.d)) for t in range(t0, t1)])
+        v = np.stack([self._step(seed, T_DEC_V, t, (self.B, self.Hkv, self.d)) for t in range(t0, t1)])
+        return k, v
 
     def with_(self, **kw) -> "DecodeWorkload":
         d = dict(self.__dict__)

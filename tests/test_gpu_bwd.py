@@ -1,0 +1,123 @@
+"""Backward on the GPU against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sepllm_oracle as orc
+from separator_kv_cache_amd import binding as sa
+from separator_kv_cache_amd import synth
+from tests.util import TOL_BF16, as_f64, inputs, max_abs, say, tol_bf16_edge
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, seed=0):
+    tok_d, (q, k, v), host, tok = inputs(wl, seed)
+    do = torch.from_numpy(wl.dout(seed)).to(torch.bfloat16)
+    m = sa.build_mask(tok_d, synth.SEP_IDS, wl.a, wl.n)
+    sc = 1.0 / math.sqrt(wl.d)
+    o, lse = sa.sepattn_fwd(q, k, v, m, sc)
+    dq, dk, dv = sa.sepattn_bwd(q, k, v, o, lse, do.cuda(), m, sc)
+    torch.cuda.synchronize()
+    f = orc.separator_flags(tok, synth.SEP_IDS)
+    return (dq, dk, dv), host + (as_f64(do),), f, (o, lse)
+
+
+@pytest.mark.parametrize("wl", synth.PYTHIA_BWD, ids=lambda w: w.name)
+def test_bwd_pythia_shape(wl):
+    say("bwd", wl.name)
+    (dq, dk, dv), (q, k, v, do), f, _ = _run(wl)
+    dqg, dkg, dvg = as_f64(dq), as_f64(dk), as_f64(dv)
+    sc = 1 / math.sqrt(wl.d)
+    for b, h in ((0, 0), (3, 5), (wl.B - 1, wl.Hq - 1)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = orc.attn_bwd(q[sl], k[sl], v[sl], do[sl], f[b:b + 1], wl.a, wl.n, sc)
+        for name, got, ref in (("dq", dqg[b, h], rq[0, 0]), ("dk", dkg[b, h], rk[0, 0]),
+                               ("dv", dvg[b, h], rv[0, 0])):
+            err = max_abs(got, ref)
+            print(wl.name, name, b, h, "max-abs", err)
+            assert err <= TOL_BF16, (name, b, h)
+    # invariants over every (sequence, head): rows of P sum to one, so the
+    # keys' dV sum to the rows' dO, and the keys' dK sum to zero
+    np.testing.assert_allclose(dvg.sum(axis=2), do.sum(axis=2), atol=0.5)
+    assert np.abs(dkg.sum(axis=2)).max() < 0.5
+
+
+def test_bwd_llama_prefill_full_size():
+    wl = synth.LLAMA_PREFILL
+    say("bwd", wl.name)
+    (dq, dk, dv), (q, k, v, do), f, _ = _run(wl)
+    dqg, dkg, dvg = as_f64(dq), as_f64(dk), as_f64(dv)
+    assert np.isfinite(dqg).all() and np.isfinite(dkg).all() and np.isfinite(dvg).all()
+    sc = 1 / math.sqrt(wl.d)
+    g = wl.Hq // wl.Hkv
+    # invariants at full size, every KV head
+    for kh in range(wl.Hkv):
+        want = do[0, kh * g:(kh + 1) * g].sum(axis=(0, 1))
+        assert max_abs(dvg[0, kh].sum(axis=0), want) < 1.0, kh
+        assert np.abs(dkg[0, kh].sum(axis=0)).max() < 1.0, kh
+    # sampled dQ rows of every q head
+    rng = np.random.default_rng(2)
+    for h in range(wl.Hq):
+        rows = np.concatenate([[0, 4, 4096, wl.L - 1], rng.integers(0, wl.L, 3)])
+        rq = orc.attn_bwd_rows(q, k, v, do, f, wl.a, wl.n, sc, 0, h, rows)
+        assert max_abs(dqg[0, h, rows], rq) <= TOL_BF16, h
+    # one whole KV group (4 q heads, 1 KV head) against the oracle
+    kh = wl.Hkv - 1
+    hs = slice(kh * g, (kh + 1) * g)
+    rq, rk, rv = orc.attn_bwd(q[:, hs], k[:, kh:kh + 1], v[:, kh:kh + 1], do[:, hs], f, wl.a, wl.n, sc,
+                              block=512)
+    assert max_abs(dqg[:, hs], rq) <= TOL_BF16
+    assert max_abs(dkg[:, kh:kh + 1], rk) <= TOL_BF16
+    assert max_abs(dvg[:, kh:kh + 1], rv) <= TOL_BF16
+
+
+EDGE = [
+    # B, Hq, Hkv, L, d, a, n, p
+    (2, 4, 2, 333, 128, 4, 40, 0.15),
+    (1, 2, 1, 1, 64, 4, 1, 0.5),
+    (2, 2, 2, 300, 64, 0, 1, 0.2),
+    (1, 3, 1, 97, 128, 200, 5, 0.3),
+    (1, 2, 2, 200, 64, 4, 200, 0.3),
+    (2, 4, 1, 257, 64, 4, 8, 1.0),
+    (2, 4, 1, 257, 128, 4, 8, 0.0),
+    (1, 8, 2, 700, 128, 2, 300, 0.12),
+    (1, 2, 1, 1500, 64, 4, 1000, 0.05),
+    (1, 2, 2, 129, 64, 1, 3, 0.4),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"edge{i}" for i in range(len(EDGE))])
+def test_bwd_edge_cases(case):
+    B, Hq, Hkv, L, d, a, n, p = case
+    say("bwd-edge", case)
+    wl = synth.PrefillWorkload("edge", 52, B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, a=a, n=n, p=p, dtype="bf16",
+                               qkv_scale=0.5)
+    (dq, dk, dv), (q, k, v, do), f, _ = _run(wl, seed=5)
+    rq, rk, rv = orc.attn_bwd(q, k, v, do, f, a, n, 1 / math.sqrt(d))
+    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        err = max_abs(as_f64(got), ref)
+        print(name, "max-abs", err, "max |ref|", float(np.abs(ref).max()))
+        assert err <= tol_bf16_edge(ref), name
+
+
+def test_bwd_deterministic_and_strided():
+    B, Hq, Hkv, L, d, a, n = 2, 4, 2, 400, 128, 4, 64
+    wl = synth.PrefillWorkload("strided", 53, B=B, Hq=Hq, Hkv=Hkv, L=L, d=d, a=a, n=n, p=0.2, dtype="bf16",
+                               qkv_scale=0.5)
+    say("bwd-strided")
+    (dq1, dk1, dv1), _, _, (o, lse) = _run(wl, seed=6)
+    (dq2, dk2, dv2), (q, k, v, do), f, _ = _run(wl, seed=6)
+    assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    qd, kd, vd = (torch.from_numpy(x).to(torch.bfloat16).cuda() for x in (q, k, v))
+    perm = lambda t: t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    dod = perm(torch.from_numpy(do).to(torch.bfloat16).cuda())
+    tok_d = torch.from_numpy(wl.tokens(6)).cuda()
+    m = sa.build_mask(tok_d, synth.SEP_IDS, a, n)
+    qs, ks, vs = perm(qd), perm(kd), perm(vd)
+    os_ = perm(o)
+    dq3, dk3, dv3 = sa.sepattn_bwd(qs, ks, vs, os_, lse, dod, m)
+    torch.cuda.synchronize()
+    assert torch.equal(dq3, dq1) and torch.equal(dk3, dk1) and torch.equal(dv3, dv1)

@@ -1,0 +1,161 @@
+"""SepCache manager and decode on the GPU against the oracle's simulator."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sepllm_oracle as orc
+from separator_kv_cache_amd import binding as sa
+from separator_kv_cache_amd import synth
+from tests.util import TOL_BF16, as_f64, max_abs, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16)
+
+
+def _setup(wl, seed=0):
+    flags = wl.flags(seed)
+    k, v = wl.kv_steps(0, wl.T, seed)
+    kb, vb = _bf(k), _bf(v)
+    return flags, kb, vb
+
+
+def _check_state(cache, sims, kb, vb, t):
+    """Order, length and the K/V bytes of every occupied slot, bit-exact."""
+    pos, ln = cache.export_order()
+    pos, ln = pos.cpu().numpy(), ln.cpu().numpy()
+    spos = cache.slot_pos.cpu().numpy()
+    kc, vc = cache.k.cpu(), cache.v.cpu()
+    for b, sim in enumerate(sims):
+        order = sim.order()
+        assert ln[b] == len(order), (t, b)
+        assert pos[b, :len(order)].tolist() == order, (t, b)
+        assert np.all(pos[b, len(order):] == -1)
+        occ = np.nonzero(spos[b] >= 0)[0]
+        assert sorted(spos[b, occ].tolist()) == order, (t, b)
+        src = spos[b, occ]
+        assert torch.equal(kc[b][:, occ], kb[src, b].permute(1, 0, 2)), (t, b)
+        assert torch.equal(vc[b][:, occ], vb[src, b].permute(1, 0, 2)), (t, b)
+
+
+SMALL = [
+    # B, Hq, Hkv, d, a, s, n, T, p, shift, split_api
+    (3, 4, 2, 64, 2, 3, 5, 60, 0.4, True, False),
+    (3, 4, 2, 128, 2, 3, 5, 60, 0.4, False, True),
+    (2, 8, 1, 128, 0, 4, 1, 40, 0.5, True, False),
+    (2, 2, 2, 64, 4, 0, 6, 50, 0.5, True, True),
+    (2, 16, 2, 128, 3, 5, 7, 45, 1.0, True, False),
+    (2, 4, 4, 64, 1, 8, 3, 45, 0.0, False, False),
+    (1, 32, 8, 128, 4, 64, 256, 400, 0.12, True, False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"cache{i}" for i in range(len(SMALL))])
+def test_cache_steps_against_simulator(case):
+    B, Hq, Hkv, d, a, s, n, T, p, shift, split_api = case
+    say("cache", case)
+    wl = synth.DecodeWorkload("small", 70, B=B, Hq=Hq, Hkv=Hkv, d=d, a=a, s=s, n=n, T=T, p=p, shift=shift)
+    flags, kb, vb = _setup(wl)
+    qb = _bf(wl.q_steps(range(T)))
+    cache = sa.SepCache(B, Hkv, d, a, s, n, wl.theta, rope_len=max(T, a + s + n))
+    sims = [orc.SepCacheSim(a, s, n) for _ in range(B)]
+    sc = 1 / math.sqrt(d)
+    outs = []
+    for t in range(T):
+        fl = torch.from_numpy(flags[t]).cuda()
+        if split_api:
+            cache.append(kb[t].cuda(), vb[t].cuda(), fl)
+            cache.evict()
+        else:
+            cache.push(kb[t].cuda(), vb[t].cuda(), fl)
+        for b in range(B):
+            sims[b].append(int(flags[t, b]))
+            sims[b].evict()
+        outs.append(cache.decode(qb[t].cuda(), sc, shift=shift))
+        if t < 12 or t % 7 == 0 or t == T - 1:
+            torch.cuda.synchronize()
+            _check_state(cache, sims, kb, vb, t)
+    torch.cuda.synchronize()
+    ref, _ = orc.decode_run(as_f64(qb), as_f64(kb), as_f64(vb), flags, a, s, n, wl.theta, shift, sc)
+    for t in range(T):
+        assert max_abs(as_f64(outs[t]), ref[t]) <= TOL_BF16, t
+    assert int(cache.state[:, 6].abs().sum().cpu()) == 0  # no overflow flag
+
+
+def test_llama_decode_full_run_sampled():
+    wl = synth.LLAMA_DECODE
+    say("cache", wl.name)
+    flags, kb, vb = _setup(wl)
+    sample = [0, 1, 3, 4, 5, 100, 259, 260, 261, 600, 793, 1500, 2048, 4095, 6000, 8191]
+    qb = _bf(wl.q_steps(sample))
+    kd, vd = kb.cuda(), vb.cuda()
+    fd = torch.from_numpy(flags).cuda()
+    cache = sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta)
+    sims = [orc.SepCacheSim(wl.a, wl.s, wl.n) for _ in range(wl.B)]
+    sc = 1 / math.sqrt(wl.d)
+    outs = {}
+    for t in range(wl.T):
+        cache.push(kd[t], vd[t], fd[t])
+        for b in range(wl.B):
+            sims[b].append(int(flags[t, b]))
+            sims[b].evict()
+        if t in sample:
+            outs[t] = cache.decode(qb[sample.index(t)].cuda(), sc, shift=True)
+            torch.cuda.synchronize()
+            if t in (0, 5, 261, 793, 4095, 8191):
+                _check_state(cache, sims, kb, vb, t)
+    torch.cuda.synchronize()
+    assert all(len(s.order()) == wl.a + wl.s + wl.n for s in sims)
+    qfull = np.zeros((wl.T, wl.B, wl.Hq, wl.d))
+    qfull[sample] = as_f64(qb)
+    ref, _ = orc.decode_run(qfull, as_f64(kb), as_f64(vb), flags, wl.a, wl.s, wl.n, wl.theta, True, sc,
+                            out_steps=sample)
+    for t in sample:
+        assert max_abs(as_f64(outs[t]), ref[t]) <= TOL_BF16, t
+
+
+def test_cache_resume_and_determinism():
+    wl = synth.DecodeWorkload("resume", 71, B=4, Hq=8, Hkv=2, d=128, a=4, s=16, n=32, T=200, p=0.2)
+    say("cache-resume")
+    flags, kb, vb = _setup(wl)
+    qb = _bf(wl.q_steps(range(wl.T))).cuda()
+    kd, vd, fd = kb.cuda(), vb.cuda(), torch.from_numpy(flags).cuda()
+
+    def run(cache, t0, t1):
+        out = []
+        for t in range(t0, t1):
+            cache.push(kd[t], vd[t], fd[t])
+            out.append(cache.decode(qb[t]))
+        return out
+
+    c1 = sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta)
+    straight = run(c1, 0, wl.T)
+    c2 = sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta)
+    run(c2, 0, 100)
+    snap = [t.clone() for t in (c2.k, c2.v, c2.slot_pos, c2.slot_sep, c2.state)]
+    run(c2, 100, 150)  # diverge, then restore
+    for dst, src in zip((c2.k, c2.v, c2.slot_pos, c2.slot_sep, c2.state), snap):
+        dst.copy_(src)
+    resumed = run(c2, 100, wl.T)
+    torch.cuda.synchronize()
+    for t in range(100, wl.T):
+        assert torch.equal(straight[t], resumed[t - 100]), t
+
+
+def test_append_without_evict_sets_overflow_flag():
+    say("cache-overflow")
+    B, Hkv, d = 2, 2, 64
+    cache = sa.SepCache(B, Hkv, d, 1, 2, 2, 10000.0)
+    k = torch.zeros((B, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    f = torch.zeros(B, dtype=torch.uint8, device="cuda")
+    for _ in range(4):  # sink + window of 2 + spare slot, then one too many
+        cache.append(k, k, f)
+    cache.append(k, k, f)
+    torch.cuda.synchronize()
+    st = cache.state.cpu().numpy()
+    assert np.all(st[:, 6] & 1)
+    assert np.all(st[:, 0] == 4)  # the last token was not taken

@@ -388,3 +388,14 @@ def test_decode_shift_uses_ranks():
             qq = orc.rope(q_all[t, 0, h], C - 1, 10000.0)
             w = np.exp(0.5 * kk @ qq - (0.5 * kk @ qq).max())
             np.testing.assert_allclose(outs[t][0, h], (w / w.sum()) @ v_all[ordr, 0, 0], atol=1e-12)
+
+
+def test_backward_rows_match_grouped_backward():
+    B, Hq, Hkv, L, d = 1, 4, 2, 80, 8
+    q, k, v, do = (_rand((B, Hq, L, d), 30), _rand((B, Hkv, L, d), 31),
+                   _rand((B, Hkv, L, d), 32), _rand((B, Hq, L, d), 33))
+    f = orc.separator_flags(synth.tokens_iid(6, 7, B, L, 0.2), synth.SEP_IDS)
+    dq, _, _ = orc.attn_bwd(q, k, v, do, f, 3, 7, 0.3, block=9)
+    rows = [0, 1, 7, 40, 79]
+    np.testing.assert_allclose(orc.attn_bwd_rows(q, k, v, do, f, 3, 7, 0.3, 0, 3, rows), dq[0, 3, rows],
+                               atol=1e-13)

@@ -16,6 +16,15 @@ TOL_BF16 = 2e-2
 TOL_LSE_BF16 = 2e-3
 
 
+def tol_bf16_edge(ref) -> float:
+    """Bound for bf16 results on inputs outside the stated workloads, where
+    gradients can grow large (e.g. sinks absorbing all attention mass): the
+    stated 2e-2 plus 2^-8 of the largest magnitude, which covers rounding the
+    output to bf16 (2^-9 relative) and the bf16 rounding of P and dS in the
+    fp32-accumulated products (2^-9 relative per term)."""
+    return TOL_BF16 + 2.0 ** -8 * float(np.abs(np.asarray(ref)).max())
+
+
 def say(*a):
     """Names the case before each GPU step (flushed, so it survives a crash)."""
     print("[case]", *a, flush=True)
