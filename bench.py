@@ -1,0 +1,261 @@
+"""Benchmark of the SepLLM hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input:
+  prefill leg (Llama-3-8B shape: B=1, 32 q / 8 KV heads, d=128, L=32768,
+    a=4, n=4096, clustered separators at p=0.12): mask build, forward,
+    backward (dO given);
+  decode leg (Llama-3-8B shape SepCache: 16 streams, 32 q / 8 KV heads,
+    d=128, a=4, s=64, n=256, 8192 tokens per stream, separators p=0.12):
+    every token is pushed into and decoded against the cache of each of
+    `--layers` layers (32 by default, as in Llama-3-8B), so the caches'
+    working set (~680 MB) exceeds the 256 MB Infinity Cache.  Tokens run as
+    replays of a HIP graph of 64 tokens; per-token K/V/q come from a pool of
+    64 inputs, the separator flags from the workload.
+
+Prints one JSON line.  `value` is the prefill leg's kept-FLOP rate (forward
+4*d*kept + backward 10*d*kept per q head, kept pairs counted by the mask
+kernel); the decode leg's algorithmic HBM rate is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from separator_kv_cache_amd import binding as sa  # noqa: E402
+from separator_kv_cache_amd import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+CHUNK = 64                  # tokens per decode graph
+
+
+class PrefillLeg:
+    def __init__(self, wl: synth.PrefillWorkload, seed: int = 0):
+        self.wl = wl
+        dev = "cuda"
+        self.tok = torch.from_numpy(wl.tokens(seed)).to(dev)
+        q, k, v = wl.qkv(seed)
+        self.q, self.k, self.v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
+        del q, k, v
+        self.do = torch.from_numpy(wl.dout(seed)).to(torch.bfloat16).to(dev)
+        self.scale = 1.0 / math.sqrt(wl.d)
+        self.mask = sa.build_mask(self.tok, synth.SEP_IDS, wl.a, wl.n)
+        self.o, self.lse = sa.sepattn_fwd(self.q, self.k, self.v, self.mask, self.scale)
+        self.ws = None
+        torch.cuda.synchronize()
+        self.kept_per_seq = int(self.mask.kept.sum().cpu())
+        self.fwd_flops = 4.0 * wl.d * self.kept_per_seq * wl.Hq
+        self.bwd_flops = 10.0 * wl.d * self.kept_per_seq * wl.Hq
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(self):
+        wl, e = self.wl, self.ev
+        e[0].record()
+        self.mask = sa.build_mask(self.tok, synth.SEP_IDS, wl.a, wl.n)
+        e[1].record()
+        sa.sepattn_fwd(self.q, self.k, self.v, self.mask, self.scale, out=self.o, lse=self.lse)
+        e[2].record()
+        self.dq, self.dk, self.dv = sa.sepattn_bwd(self.q, self.k, self.v, self.o, self.lse, self.do,
+                                                   self.mask, self.scale, workspace=self.ws)
+        e[3].record()
+
+    def times_ms(self):
+        e = self.ev
+        return e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])
+
+
+class DecodeLeg:
+    def __init__(self, wl: synth.DecodeWorkload, layers: int, seed: int = 0):
+        self.wl, self.layers = wl, layers
+        dev = "cuda"
+        self.flags_np = wl.flags(seed)
+        self.flags = torch.from_numpy(self.flags_np).to(dev)
+        k, v = wl.kv_steps(0, CHUNK, seed)
+        self.kp = torch.from_numpy(k).to(torch.bfloat16).to(dev)
+        self.vp = torch.from_numpy(v).to(torch.bfloat16).to(dev)
+        self.qp = torch.from_numpy(wl.q_steps(range(CHUNK), seed)).to(torch.bfloat16).to(dev)
+        self.scale = 1.0 / math.sqrt(wl.d)
+        self.caches = [sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta) for _ in range(layers)]
+        self.out = torch.empty((layers, wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device=dev)
+        self.fl_static = torch.zeros((CHUNK, wl.B), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        self.stream = torch.cuda.Stream()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph, stream=self.stream):
+            for i in range(CHUNK):
+                for li, c in enumerate(self.caches):
+                    c.step(self.kp[i], self.vp[i], self.fl_static[i], self.qp[i], self.scale, shift=wl.shift,
+                           out=self.out[li])
+        torch.cuda.synchronize()
+        self.n_chunks = wl.T // CHUNK
+        assert self.n_chunks * CHUNK == wl.T
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        self.bytes = self._algorithmic_bytes()
+
+    def _algorithmic_bytes(self) -> float:
+        """Bytes the path must move: every cached K and V row read once per
+        token, plus q, o and the new K/V row (the separator move is an
+        implementation choice and not counted).  Cache lengths follow from the
+        flags: sinks, separators that left the window (at most s), window."""
+        wl = self.wl
+        T = wl.T
+        t = np.arange(T)[:, None]
+        f = self.flags_np.astype(np.int64)
+        f_after_sinks = np.where(np.arange(T)[:, None] >= wl.a, f, 0)
+        csum = np.cumsum(f_after_sinks, axis=0)  # separators at positions <= t
+        left = np.where(t - wl.n >= 0, csum[np.clip(t - wl.n, 0, None)[:, 0]], 0)  # positions <= t-n
+        length = np.minimum(t + 1, wl.a) + np.minimum(left, wl.s) + np.minimum(np.maximum(t + 1 - wl.a, 0), wl.n)
+        row = wl.Hkv * wl.d * 2
+        per_layer = float(length.sum()) * row * 2 + T * wl.B * (2 * wl.Hq * wl.d * 2 + 2 * row)
+        self.mean_len = float(length.mean())
+        return per_layer * self.layers
+
+    def step(self):
+        for c in self.caches:
+            c.reset()
+        self.ev[0].record()
+        for ch in range(self.n_chunks):
+            self.fl_static.copy_(self.flags[ch * CHUNK:(ch + 1) * CHUNK])
+            self.graph.replay()
+        self.ev[1].record()
+
+    def time_ms(self):
+        return self.ev[0].elapsed_time(self.ev[1])
+
+
+def cpu_baseline(leg: PrefillLeg, budget_s: float = 20.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the prefill
+    workload: the forward of one q head over all rows (kept keys only)."""
+    from oracle import sepllm_oracle as orc
+    wl = leg.wl
+    cores = len(os.sched_getaffinity(0))
+    q = leg.q[:, :1].float().cpu().numpy()
+    k = leg.k[:, :1].float().cpu().numpy()
+    v = leg.v[:, :1].float().cpu().numpy()
+    f = leg.mask.is_sep.cpu().numpy()
+    rows = wl.L
+    # shrink the sample if a first slice shows the budget would be exceeded
+    t0 = time.perf_counter()
+    orc.attn_fwd(q[:, :, :2048], k[:, :, :2048], v[:, :, :2048], f[:, :2048], wl.a, wl.n, leg.scale)
+    t_small = time.perf_counter() - t0
+    est = t_small * (wl.L / 2048) ** 1.6
+    if est > budget_s:
+        rows = int(2048 * (budget_s / max(t_small, 1e-3)) ** (1 / 1.6)) // 256 * 256
+        rows = max(2048, min(wl.L, rows))
+    t0 = time.perf_counter()
+    orc.attn_fwd(q[:, :, :rows], k[:, :, :rows], v[:, :, :rows], f[:, :rows], wl.a, wl.n, leg.scale)
+    dt = time.perf_counter() - t0
+    kept = int(orc.kept_pairs(f[:, :rows], wl.a, wl.n).sum())
+    flops = 4.0 * wl.d * kept
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 numpy forward of 1 of {wl.Hq} q heads, rows 0..{rows - 1} of {wl.L} "
+                      f"({kept} kept pairs, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=32, help="decode layer caches")
+    ap.add_argument("--decode-tokens", type=int, default=None,
+                    help="tokens per stream (default: the workload's 8192; fewer only for profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the SepLLM path here runs on a single MI355X "
+              "(multi-GPU sharding is a design note, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    pre = PrefillLeg(synth.LLAMA_PREFILL, args.seed)
+    dwl = synth.LLAMA_DECODE
+    if args.decode_tokens is not None:
+        dwl = dwl.with_(T=args.decode_tokens)
+    dec = DecodeLeg(dwl, args.layers, args.seed)
+
+    for _ in range(args.warmup):
+        pre.step()
+        dec.step()
+    torch.cuda.synchronize()
+
+    t_mask = t_fwd = t_bwd = t_dec = 0.0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        pre.step()
+        dec.step()
+        torch.cuda.synchronize()
+        a, b, c = pre.times_ms()
+        t_mask += a
+        t_fwd += b
+        t_bwd += c
+        t_dec += dec.time_ms()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    K = args.steps
+    t_mask, t_fwd, t_bwd, t_dec = t_mask / K, t_fwd / K, t_bwd / K, t_dec / K
+    pre_ms = t_mask + t_fwd + t_bwd
+    value = (pre.fwd_flops + pre.bwd_flops) / (pre_ms * 1e-3) / 1e12
+    fwd_tf = pre.fwd_flops / (t_fwd * 1e-3) / 1e12
+    bwd_tf = pre.bwd_flops / (t_bwd * 1e-3) / 1e12
+    dec_gbs = dec.bytes / (t_dec * 1e-3) / 1e9
+    launches = dec.wl.T * args.layers
+    wl = pre.wl
+    out = {
+        "metric": "kept-FLOP TFLOP/s (MFMA util) sep-attn prefill + decode HBM GB/s, Llama-3-8B",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama3-8b sep-attn prefill L=32768 fwd+bwd + sepcache decode 8192 tokens x "
+                        f"{args.layers} layers",
+            "prefill": {"B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "L": wl.L, "d": wl.d, "a": wl.a, "n": wl.n,
+                        "p": wl.p, "separators": "clustered"},
+            "decode": {"B": dec.wl.B, "Hq": dec.wl.Hq, "Hkv": dec.wl.Hkv, "d": dec.wl.d, "a": dec.wl.a,
+                       "s": dec.wl.s, "n": dec.wl.n, "tokens": dec.wl.T, "p": dec.wl.p,
+                       "layers": args.layers, "shift": dec.wl.shift},
+        },
+        "prefill": {
+            "kept_pairs_per_head": pre.kept_per_seq,
+            "kept_fraction_of_causal": round(pre.kept_per_seq / (wl.L * (wl.L + 1) / 2), 4),
+            "mask_ms": round(t_mask, 4), "fwd_ms": round(t_fwd, 4), "bwd_ms": round(t_bwd, 4),
+            "fwd_tflops": round(fwd_tf, 2), "bwd_tflops": round(bwd_tf, 2),
+            "fwd_util": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "bwd_util": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+        },
+        "decode": {
+            "ms": round(t_dec, 3), "gbs": round(dec_gbs, 1), "frac_of_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "bytes": dec.bytes, "mean_cache_len": round(dec.mean_len, 2), "launches": launches,
+            "us_per_token_layer": round(t_dec * 1e3 / (dec.wl.T * args.layers), 3),
+        },
+        "roofline": {
+            "kernel": "sepattn forward (fwd_kernel bf16 d=128)",
+            "bound": "mfma", "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(pre)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

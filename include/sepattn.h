@@ -161,32 +161,30 @@ SEPATTN_API int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mas
  * ascending original position.
  *
  * All streams of a batch share the step: stream b appends its own token and
- * flag.  Physical slots per stream: [0, a) sinks, [a, a+s) separator ring,
- * [a+s, a+s+n+1) window ring (one spare slot for the appended token).
+ * flag.  Physical slots per stream and KV head: [0, a) sinks, [a, a+s)
+ * separator ring, [a+s, a+s+n+1) window ring (one spare slot for the
+ * appended token).  Every KV head keeps its own copy of the slot metadata and
+ * counters (all copies hold the same values), so the work of one (stream, KV
+ * head) never waits on another workgroup.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int B, Hkv, d;       /* streams, KV heads, head dim (64 or 128)              */
   int a, s, n;         /* sinks, separator capacity (>= 0), window (>= 1)       */
   void* k;             /* bf16 [B, Hkv, slots, d] keys before RoPE              */
   void* v;             /* bf16 [B, Hkv, slots, d]                               */
-  int32_t* slot_pos;   /* [B, slots] original position held, -1 if empty        */
-  uint8_t* slot_sep;   /* [B, slots] separator flag of the token held           */
-  int32_t* state;      /* [B, 8] counters: tokens seen, sinks, sep head, sep
-                          count, window head, window count, 2 reserved          */
-  const float* rope;   /* fp32 [rope_len, d/2, 2] (cos, sin) from
-                          sepcache_rope_table                                   */
-  int rope_len;        /* positions covered by the table                        */
+  int32_t* slot_pos;   /* [B, Hkv, slots] original position held, -1 if empty  */
+  uint8_t* slot_sep;   /* [B, Hkv, slots] separator flag of the token held     */
+  int32_t* state;      /* [B, Hkv, 8] counters: tokens seen, sinks, sep head,
+                          sep count, window head, window count, flags (bit 0:
+                          an append found the window full and was dropped),
+                          separator flag of the window's oldest entry          */
+  float theta;         /* RoPE base: pair (i, i + d/2) turns by p * theta^(-2i/d)
+                          at position p                                        */
 } sepcache;
 
 /* Physical slots per stream and KV head: a + s + n + 1. */
 SEPATTN_API int sepcache_slots(int a, int s, int n);
-/* Fill a device fp32 table [len, d/2, 2] with cos and sin of p * w_i,
- * w_i = theta^(-2i/d) (half-split RoPE pairing dimension i with i + d/2),
- * computed in double precision on the host.  Position shifting needs
- * len >= a + s + n; original positions need len > the largest position.
- * Copies synchronously. */
-SEPATTN_API int sepcache_rope_table(float* table, int len, int d, float theta, void* stream);
-/* Empty every stream (slot_pos = -1, counters 0). */
+/* Empty every stream (slot_pos = -1, counters 0) of every KV head. */
 SEPATTN_API int sepcache_reset(const sepcache* c, void* stream);
 /* Append token t of every stream: k_new, v_new bf16 [B, Hkv, d] contiguous,
  * is_sep device uint8 [B].  Token t < a becomes a sink, later tokens enter the
@@ -204,16 +202,28 @@ SEPATTN_API int sepcache_push(const sepcache* c, const void* k_new, const void* 
  * own, softmax(scale * q.k) over every entry, times V.  shift != 0: positions
  * are ranks in the logical order (the query is the last rank, [HUB] A1);
  * shift == 0: original token positions.
- *   q bf16 [B, Hq, d] (before RoPE), o bf16 [B, Hq, d], contiguous.
- *   workspace: sepcache_decode_workspace_size() bytes of device memory,
- *   zero-filled by the caller before its first use; each call leaves its
- *   counters at zero again.  Calls that share a workspace must not overlap.
- * A query or key position outside the RoPE table (possible only without
- * shifting, when the table is shorter than the stream) makes that output NaN.
+ *   q bf16 [B, Hq, d] (before RoPE), o bf16 [B, Hq, d], contiguous;
+ *   Hq / Hkv in {1, 2, 4, 8}.
+ * RoPE angles are computed on the device with the position times the
+ * frequency reduced modulo one turn in double precision, so any position is
+ * exact to fp32 rounding of the reduced angle.  The cache is only read.
+ * Caches of up to 384 (d = 128) or 768 (d = 64) slots run as one kernel with
+ * one workgroup per (stream, KV head) and need no workspace; larger caches
+ * split the slots over several workgroups and merge their partial results in
+ * a second kernel.  workspace: sepcache_decode_workspace_size() bytes of
+ * device memory (0 for the one-kernel case, where NULL is accepted; no
+ * initialisation needed); calls that share a workspace must not overlap.
  * Decode before any append writes zeros. */
 SEPATTN_API size_t sepcache_decode_workspace_size(const sepcache* c, int Hq);
 SEPATTN_API int sepcache_decode(const sepcache* c, int Hq, const void* q, float scale, int shift,
                     void* o, void* workspace, size_t workspace_bytes, void* stream);
+/* One decode step: append the new token (k_new, v_new, is_sep as for
+ * sepcache_append), evict, and attend (q, o, workspace as for
+ * sepcache_decode); the same result as sepcache_push then sepcache_decode,
+ * in two launches that read the cache once. */
+SEPATTN_API int sepcache_step(const sepcache* c, const void* k_new, const void* v_new,
+                  const uint8_t* is_sep, int Hq, const void* q, float scale, int shift,
+                  void* o, void* workspace, size_t workspace_bytes, void* stream);
 /* Original positions in logical order: pos [B, a+s+n] (unused tail -1),
  * len [B] entries held.  For bit-exact checks against a reference. */
 SEPATTN_API int sepcache_export_order(const sepcache* c, int32_t* pos, int32_t* len, void* stream);

@@ -29,7 +29,7 @@ class SepattnShape(ctypes.Structure):
 class SepCacheStruct(ctypes.Structure):
     _fields_ = [("B", c_int), ("Hkv", c_int), ("d", c_int), ("a", c_int), ("s", c_int), ("n", c_int),
                 ("k", c_void_p), ("v", c_void_p), ("slot_pos", c_void_p), ("slot_sep", c_void_p),
-                ("state", c_void_p), ("rope", c_void_p), ("rope_len", c_int)]
+                ("state", c_void_p), ("theta", c_float)]
 
 
 _SIGS = {
@@ -46,7 +46,6 @@ _SIGS = {
                             c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                             c_void_p, c_void_p, c_size_t, c_void_p]),
     "sepcache_slots": (c_int, [c_int, c_int, c_int]),
-    "sepcache_rope_table": (c_int, [c_void_p, c_int, c_int, c_float, c_void_p]),
     "sepcache_reset": (c_int, [POINTER(SepCacheStruct), c_void_p]),
     "sepcache_append": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, c_void_p, c_void_p]),
     "sepcache_evict": (c_int, [POINTER(SepCacheStruct), c_void_p]),
@@ -55,6 +54,8 @@ _SIGS = {
     "sepcache_decode": (c_int, [POINTER(SepCacheStruct), c_int, c_void_p, c_float, c_int, c_void_p,
                                 c_void_p, c_size_t, c_void_p]),
     "sepcache_export_order": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, c_void_p]),
+    "sepcache_step": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_float,
+                              c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
 }
 
 EXPORTED = tuple(_SIGS)

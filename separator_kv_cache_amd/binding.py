@@ -132,10 +132,10 @@ def sepattn_bwd(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, work
 
 
 class SepCache:
-    """A SepCache for B streams (bf16 K/V) plus its RoPE table."""
+    """A SepCache for B streams (bf16 K/V)."""
 
     def __init__(self, B: int, Hkv: int, d: int, a: int, s: int, n: int, theta: float = 500000.0,
-                 rope_len: int | None = None, device="cuda"):
+                 device="cuda"):
         lib = _lib.load()
         slots = lib.sepcache_slots(a, s, n)
         if slots < 0:
@@ -143,18 +143,15 @@ class SepCache:
         self.B, self.Hkv, self.d, self.a, self.s, self.n, self.slots = B, Hkv, d, a, s, n, slots
         self.k = torch.zeros((B, Hkv, slots, d), dtype=torch.bfloat16, device=device)
         self.v = torch.zeros((B, Hkv, slots, d), dtype=torch.bfloat16, device=device)
-        self.slot_pos = torch.empty((B, slots), dtype=torch.int32, device=device)
-        self.slot_sep = torch.empty((B, slots), dtype=torch.uint8, device=device)
-        self.state = torch.empty((B, 8), dtype=torch.int32, device=device)
-        self.rope_len = a + s + n if rope_len is None else rope_len
-        self.rope = torch.empty((self.rope_len, d // 2, 2), dtype=torch.float32, device=device)
-        check(lib.sepcache_rope_table(_ptr(self.rope), self.rope_len, d, float(theta), _stream()))
+        self.slot_pos = torch.empty((B, Hkv, slots), dtype=torch.int32, device=device)
+        self.slot_sep = torch.empty((B, Hkv, slots), dtype=torch.uint8, device=device)
+        self.state = torch.empty((B, Hkv, 8), dtype=torch.int32, device=device)
         c = SepCacheStruct()
         c.B, c.Hkv, c.d, c.a, c.s, c.n = B, Hkv, d, a, s, n
         c.k, c.v = self.k.data_ptr(), self.v.data_ptr()
         c.slot_pos, c.slot_sep, c.state = (self.slot_pos.data_ptr(), self.slot_sep.data_ptr(),
                                            self.state.data_ptr())
-        c.rope, c.rope_len = self.rope.data_ptr(), self.rope_len
+        c.theta = float(theta)
         self.c = c
         self._ws = None
         self.reset()
@@ -183,20 +180,34 @@ class SepCache:
     def workspace(self, Hq: int) -> torch.Tensor:
         need = _lib.load().sepcache_decode_workspace_size(ctypes.byref(self.c), Hq)
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=self.k.device)
+            self._ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.k.device)
         return self._ws
 
     def decode(self, q, scale: float | None = None, shift: bool = True, out=None):
         """sepcache_decode: q bf16 [B, Hq, d] -> o bf16 [B, Hq, d]."""
-        if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[0] != self.B or not q.is_contiguous():
-            raise ValueError("q must be contiguous bf16 [B, Hq, d]")
-        Hq = q.shape[1]
-        o = torch.empty_like(q) if out is None else out
-        ws = self.workspace(Hq)
+        o = self._q_out(q, out)
+        ws = self.workspace(q.shape[1])
         sc = 1.0 / math.sqrt(self.d) if scale is None else float(scale)
-        check(_lib.load().sepcache_decode(ctypes.byref(self.c), Hq, _ptr(q), sc, 1 if shift else 0, _ptr(o),
-                                          _ptr(ws), ws.numel(), _stream()))
+        check(_lib.load().sepcache_decode(ctypes.byref(self.c), q.shape[1], _ptr(q), sc, 1 if shift else 0,
+                                          _ptr(o), _ptr(ws), ws.numel(), _stream()))
         return o
+
+    def step(self, k_new, v_new, is_sep, q, scale: float | None = None, shift: bool = True, out=None):
+        """sepcache_step: append + evict + decode."""
+        self._kvf(k_new, v_new, is_sep)
+        o = self._q_out(q, out)
+        ws = self.workspace(q.shape[1])
+        sc = 1.0 / math.sqrt(self.d) if scale is None else float(scale)
+        check(_lib.load().sepcache_step(ctypes.byref(self.c), _ptr(k_new), _ptr(v_new), _ptr(is_sep), q.shape[1],
+                                        _ptr(q), sc, 1 if shift else 0, _ptr(o), _ptr(ws), ws.numel(),
+                                        _stream()))
+        return o
+
+    def _q_out(self, q, out):
+        if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[0] != self.B or q.shape[2] != self.d \
+                or not q.is_contiguous():
+            raise ValueError("q must be contiguous bf16 [B, Hq, d]")
+        return torch.empty_like(q) if out is None else out
 
     def export_order(self):
         """sepcache_export_order: (pos int32 [B, a+s+n], len int32 [B])."""

@@ -27,6 +27,8 @@ size_t sepcache_decode_ws_bytes(const sepcache* c, int Hq);
 int sepcache_launch_decode(const sepcache* c, int Hq, const void* q, float scale, int shift, void* o,
                            void* ws, hipStream_t st);
 int sepcache_launch_export(const sepcache* c, int32_t* pos, int32_t* len, hipStream_t st);
+int sepcache_launch_step(const sepcache* c, const void* k_new, const void* v_new, const uint8_t* is_sep, int Hq,
+                         const void* q, float scale, int shift, void* o, void* ws, hipStream_t st);
 
 static thread_local char g_err[512] = "";
 
@@ -194,7 +196,7 @@ int sepcache_slots(int a, int s, int n) {
   return a + s + n + 1;
 }
 
-static int check_cache(const sepcache* c, const char* who, bool need_rope) {
+static int check_cache(const sepcache* c, const char* who) {
   if (!c) return sepattn_fail(SEPATTN_EINVAL, "%s: null cache", who);
   if (c->B <= 0 || c->Hkv <= 0) return sepattn_fail(SEPATTN_EINVAL, "%s: B=%d Hkv=%d", who, c->B, c->Hkv);
   if (c->d != 64 && c->d != 128) return sepattn_fail(SEPATTN_ENOTSUP, "%s: head dim %d (64 or 128)", who, c->d);
@@ -204,35 +206,13 @@ static int check_cache(const sepcache* c, const char* who, bool need_rope) {
   if (!c->k || !c->v || !c->slot_pos || !c->slot_sep || !c->state)
     return sepattn_fail(SEPATTN_EINVAL, "%s: null cache array", who);
   if (!aligned16(c->k) || !aligned16(c->v)) return sepattn_fail(SEPATTN_EINVAL, "%s: K/V not 16-byte aligned", who);
-  if (need_rope && (!c->rope || c->rope_len < 1)) return sepattn_fail(SEPATTN_EINVAL, "%s: no RoPE table", who);
+  if (!(c->theta > 1.f) || !std::isfinite(c->theta)) return sepattn_fail(SEPATTN_EINVAL, "%s: theta=%g", who, c->theta);
   return SEPATTN_OK;
-}
-
-int sepcache_rope_table(float* table, int len, int d, float theta, void* stream) {
-  g_err[0] = 0;
-  if (!table) return sepattn_fail(SEPATTN_EINVAL, "rope_table: null table");
-  if (len < 1 || (d != 64 && d != 128)) return sepattn_fail(SEPATTN_EINVAL, "rope_table: len=%d d=%d", len, d);
-  if (!(theta > 1.f) || !std::isfinite(theta)) return sepattn_fail(SEPATTN_EINVAL, "rope_table: theta=%g", theta);
-  SEPATTN_TRY(sepattn_check_device());
-  const int half = d / 2;
-  std::vector<float> host((size_t)len * half * 2);
-  for (int i = 0; i < half; ++i) {
-    const double w = std::pow((double)theta, -2.0 * i / d);
-    for (int p = 0; p < len; ++p) {
-      const double ang = (double)p * w;
-      host[((size_t)p * half + i) * 2 + 0] = (float)std::cos(ang);
-      host[((size_t)p * half + i) * 2 + 1] = (float)std::sin(ang);
-    }
-  }
-  hipStream_t st = (hipStream_t)stream;
-  SEPATTN_TRY(sepattn_hip_check(hipMemcpyAsync(table, host.data(), host.size() * 4, hipMemcpyHostToDevice, st),
-                                "rope_table copy"));
-  return sepattn_hip_check(hipStreamSynchronize(st), "rope_table sync");
 }
 
 int sepcache_reset(const sepcache* c, void* stream) {
   g_err[0] = 0;
-  SEPATTN_TRY(check_cache(c, "reset", false));
+  SEPATTN_TRY(check_cache(c, "reset"));
   SEPATTN_TRY(sepattn_check_device());
   return sepcache_launch_reset(c, (hipStream_t)stream);
 }
@@ -240,7 +220,7 @@ int sepcache_reset(const sepcache* c, void* stream) {
 static int update(const sepcache* c, const void* k_new, const void* v_new, const uint8_t* is_sep, int app,
                   int ev, void* stream, const char* who) {
   g_err[0] = 0;
-  SEPATTN_TRY(check_cache(c, who, false));
+  SEPATTN_TRY(check_cache(c, who));
   if (app && (!k_new || !v_new || !is_sep)) return sepattn_fail(SEPATTN_EINVAL, "%s: null input", who);
   if (app && (!aligned16(k_new) || !aligned16(v_new)))
     return sepattn_fail(SEPATTN_EINVAL, "%s: K/V rows not 16-byte aligned", who);
@@ -257,33 +237,57 @@ int sepcache_push(const sepcache* c, const void* k_new, const void* v_new, const
 }
 
 size_t sepcache_decode_workspace_size(const sepcache* c, int Hq) {
-  if (!c || c->B <= 0 || c->Hkv <= 0 || Hq <= 0) return 0;
+  if (!c || c->B <= 0 || c->Hkv <= 0 || Hq <= 0 || Hq % c->Hkv != 0 || (c->d != 64 && c->d != 128) ||
+      c->a < 0 || c->s < 0 || c->n < 1)
+    return 0;
   return sepcache_decode_ws_bytes(c, Hq);
+}
+
+static int check_attend(const sepcache* c, int Hq, const void* q, float scale, int shift, void* o, const char* who) {
+  SEPATTN_TRY(check_cache(c, who));
+  if (Hq <= 0 || Hq % c->Hkv != 0)
+    return sepattn_fail(SEPATTN_EINVAL, "%s: Hq=%d is not a positive multiple of Hkv=%d", who, Hq, c->Hkv);
+  const int G = Hq / c->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return sepattn_fail(SEPATTN_ENOTSUP, "%s: %d q heads per KV head (1, 2, 4 or 8)", who, G);
+  if (!q || !o) return sepattn_fail(SEPATTN_EINVAL, "%s: null q or o", who);
+  if (!aligned16(q) || !aligned16(o)) return sepattn_fail(SEPATTN_EINVAL, "%s: q/o not 16-byte aligned", who);
+  if (!std::isfinite(scale)) return sepattn_fail(SEPATTN_EINVAL, "%s: scale is not finite", who);
+  return SEPATTN_OK;
+}
+
+static int check_ws(const sepcache* c, int Hq, const void* ws, size_t bytes, const char* who) {
+  const size_t need = sepcache_decode_ws_bytes(c, Hq);
+  if (need == 0) return SEPATTN_OK;  // the single-kernel path uses none
+  if (!ws || bytes < need) return sepattn_fail(SEPATTN_ESPACE, "%s: workspace %zu bytes < %zu", who, bytes, need);
+  if (!aligned16(ws)) return sepattn_fail(SEPATTN_EINVAL, "%s: workspace not 16-byte aligned", who);
+  return SEPATTN_OK;
 }
 
 int sepcache_decode(const sepcache* c, int Hq, const void* q, float scale, int shift, void* o, void* workspace,
                     size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  SEPATTN_TRY(check_cache(c, "decode", true));
-  if (Hq <= 0 || Hq % c->Hkv != 0)
-    return sepattn_fail(SEPATTN_EINVAL, "decode: Hq=%d is not a positive multiple of Hkv=%d", Hq, c->Hkv);
-  if (Hq / c->Hkv > 8) return sepattn_fail(SEPATTN_ENOTSUP, "decode: more than 8 q heads per KV head");
-  if (!q || !o) return sepattn_fail(SEPATTN_EINVAL, "decode: null q or o");
-  if (!aligned16(q) || !aligned16(o)) return sepattn_fail(SEPATTN_EINVAL, "decode: q/o not 16-byte aligned");
-  if (!std::isfinite(scale)) return sepattn_fail(SEPATTN_EINVAL, "decode: scale is not finite");
-  const size_t need = sepcache_decode_ws_bytes(c, Hq);
-  if (need && (!workspace || workspace_bytes < need))
-    return sepattn_fail(SEPATTN_ESPACE, "decode: workspace %zu bytes < %zu", workspace_bytes, need);
-  if (shift && c->rope_len < c->a + c->s + c->n)
-    return sepattn_fail(SEPATTN_EINVAL, "decode: RoPE table of %d positions < a+s+n=%d", c->rope_len,
-                        c->a + c->s + c->n);
+  SEPATTN_TRY(check_attend(c, Hq, q, scale, shift, o, "decode"));
+  SEPATTN_TRY(check_ws(c, Hq, workspace, workspace_bytes, "decode"));
   SEPATTN_TRY(sepattn_check_device());
   return sepcache_launch_decode(c, Hq, q, scale, shift, o, workspace, (hipStream_t)stream);
 }
 
+int sepcache_step(const sepcache* c, const void* k_new, const void* v_new, const uint8_t* is_sep, int Hq,
+                  const void* q, float scale, int shift, void* o, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  g_err[0] = 0;
+  SEPATTN_TRY(check_attend(c, Hq, q, scale, shift, o, "step"));
+  if (!k_new || !v_new || !is_sep) return sepattn_fail(SEPATTN_EINVAL, "step: null input");
+  if (!aligned16(k_new) || !aligned16(v_new)) return sepattn_fail(SEPATTN_EINVAL, "step: K/V rows not 16-byte aligned");
+  SEPATTN_TRY(check_ws(c, Hq, workspace, workspace_bytes, "step"));
+  SEPATTN_TRY(sepattn_check_device());
+  return sepcache_launch_step(c, k_new, v_new, is_sep, Hq, q, scale, shift, o, workspace, (hipStream_t)stream);
+}
+
 int sepcache_export_order(const sepcache* c, int32_t* pos, int32_t* len, void* stream) {
   g_err[0] = 0;
-  SEPATTN_TRY(check_cache(c, "export_order", false));
+  SEPATTN_TRY(check_cache(c, "export_order"));
   if (!pos || !len) return sepattn_fail(SEPATTN_EINVAL, "export_order: null output");
   SEPATTN_TRY(sepattn_check_device());
   return sepcache_launch_export(c, pos, len, (hipStream_t)stream);

@@ -29,6 +29,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -65,3 +66,23 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Data-parallel-primitive moves within a row of 16 lanes (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within 16
+
+// Sum over aligned groups of N lanes (N = 4, 8 or 16); every lane gets it.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp_mov<DPP_XOR1>(x);
+  x += dpp_mov<DPP_XOR2>(x);
+  if constexpr (N >= 8) x += dpp_mov<DPP_HALF_MIRROR>(x);
+  if constexpr (N >= 16) x += dpp_mov<DPP_MIRROR>(x);
+  return x;
+}

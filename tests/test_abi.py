@@ -99,11 +99,14 @@ def test_argument_validation_without_gpu():
     c.d = 64
     assert lib.sepcache_reset(ctypes.byref(c), None) == _lib.EINVAL  # null arrays
     c.k = c.v = c.slot_pos = c.slot_sep = c.state = 4096
-    assert lib.sepcache_decode(ctypes.byref(c), 3, p, 0.1, 1, p, p, 10 ** 6, None) == _lib.EINVAL  # no rope
-    c.rope, c.rope_len = 4096, 100
+    assert lib.sepcache_decode(ctypes.byref(c), 4, p, 0.1, 1, p, p, 10 ** 6, None) == _lib.EINVAL  # theta 0
+    c.theta = 10000.0
     assert lib.sepcache_decode(ctypes.byref(c), 3, p, 0.1, 1, p, p, 10 ** 6, None) == _lib.EINVAL
     assert lib.sepcache_decode(ctypes.byref(c), 32, p, 0.1, 1, p, p, 10 ** 6, None) == _lib.ENOTSUP
-    c.rope_len = 10
-    assert lib.sepcache_decode(ctypes.byref(c), 4, p, 0.1, 1, p, p, 10 ** 6, None) == _lib.EINVAL
-    assert lib.sepcache_rope_table(None, 10, 64, 10000.0, None) == _lib.EINVAL
-    assert lib.sepcache_rope_table(p, 10, 64, 0.5, None) == _lib.EINVAL
+    assert lib.sepcache_decode_workspace_size(ctypes.byref(c), 4) == 0  # small cache: one kernel
+    c.s = 2000  # large cache: split path with a workspace
+    need = lib.sepcache_decode_workspace_size(ctypes.byref(c), 4)
+    assert need > 0
+    assert lib.sepcache_decode(ctypes.byref(c), 4, p, 0.1, 1, p, p, need - 1, None) == _lib.ESPACE
+    c.s = 8
+    assert lib.sepcache_step(ctypes.byref(c), None, p, p, 4, p, 0.1, 1, p, None, 0, None) == _lib.EINVAL

@@ -28,54 +28,64 @@ def _check_state(cache, sims, kb, vb, t):
     """Order, length and the K/V bytes of every occupied slot, bit-exact."""
     pos, ln = cache.export_order()
     pos, ln = pos.cpu().numpy(), ln.cpu().numpy()
-    spos = cache.slot_pos.cpu().numpy()
+    spos = cache.slot_pos.cpu().numpy()          # [B, Hkv, slots]
+    state = cache.state.cpu().numpy()
     kc, vc = cache.k.cpu(), cache.v.cpu()
     for b, sim in enumerate(sims):
         order = sim.order()
         assert ln[b] == len(order), (t, b)
         assert pos[b, :len(order)].tolist() == order, (t, b)
         assert np.all(pos[b, len(order):] == -1)
-        occ = np.nonzero(spos[b] >= 0)[0]
-        assert sorted(spos[b, occ].tolist()) == order, (t, b)
-        src = spos[b, occ]
-        assert torch.equal(kc[b][:, occ], kb[src, b].permute(1, 0, 2)), (t, b)
-        assert torch.equal(vc[b][:, occ], vb[src, b].permute(1, 0, 2)), (t, b)
+        for h in range(cache.Hkv):
+            assert np.array_equal(state[b, h], state[b, 0]), (t, b, h)
+            occ = np.nonzero(spos[b, h] >= 0)[0]
+            assert sorted(spos[b, h, occ].tolist()) == order, (t, b, h)
+            src = spos[b, h, occ]
+            assert torch.equal(kc[b, h, occ], kb[src, b, h]), (t, b, h)
+            assert torch.equal(vc[b, h, occ], vb[src, b, h]), (t, b, h)
 
 
 SMALL = [
-    # B, Hq, Hkv, d, a, s, n, T, p, shift, split_api
-    (3, 4, 2, 64, 2, 3, 5, 60, 0.4, True, False),
-    (3, 4, 2, 128, 2, 3, 5, 60, 0.4, False, True),
-    (2, 8, 1, 128, 0, 4, 1, 40, 0.5, True, False),
-    (2, 2, 2, 64, 4, 0, 6, 50, 0.5, True, True),
-    (2, 16, 2, 128, 3, 5, 7, 45, 1.0, True, False),
-    (2, 4, 4, 64, 1, 8, 3, 45, 0.0, False, False),
-    (1, 32, 8, 128, 4, 64, 256, 400, 0.12, True, False),
+    # B, Hq, Hkv, d, a, s, n, T, p, shift, api ("push", "split" = append+evict, "step" = fused)
+    (3, 4, 2, 64, 2, 3, 5, 60, 0.4, True, "push"),
+    (3, 4, 2, 128, 2, 3, 5, 60, 0.4, False, "split"),
+    (3, 4, 2, 128, 2, 3, 5, 60, 0.4, False, "step"),
+    (2, 8, 1, 128, 0, 4, 1, 40, 0.5, True, "step"),
+    (2, 2, 2, 64, 4, 0, 6, 50, 0.5, True, "split"),
+    (2, 16, 2, 128, 3, 5, 7, 45, 1.0, True, "push"),
+    (2, 16, 2, 128, 3, 5, 7, 45, 1.0, True, "step"),
+    (2, 4, 4, 64, 1, 8, 3, 45, 0.0, False, "push"),
+    (2, 8, 2, 64, 4, 200, 300, 700, 0.3, True, "step"),
+    (1, 32, 8, 128, 4, 64, 256, 400, 0.12, True, "push"),
+    (1, 32, 8, 128, 4, 64, 256, 400, 0.12, True, "step"),
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[f"cache{i}" for i in range(len(SMALL))])
 def test_cache_steps_against_simulator(case):
-    B, Hq, Hkv, d, a, s, n, T, p, shift, split_api = case
+    B, Hq, Hkv, d, a, s, n, T, p, shift, api = case
     say("cache", case)
     wl = synth.DecodeWorkload("small", 70, B=B, Hq=Hq, Hkv=Hkv, d=d, a=a, s=s, n=n, T=T, p=p, shift=shift)
     flags, kb, vb = _setup(wl)
     qb = _bf(wl.q_steps(range(T)))
-    cache = sa.SepCache(B, Hkv, d, a, s, n, wl.theta, rope_len=max(T, a + s + n))
+    cache = sa.SepCache(B, Hkv, d, a, s, n, wl.theta)
     sims = [orc.SepCacheSim(a, s, n) for _ in range(B)]
     sc = 1 / math.sqrt(d)
     outs = []
     for t in range(T):
         fl = torch.from_numpy(flags[t]).cuda()
-        if split_api:
-            cache.append(kb[t].cuda(), vb[t].cuda(), fl)
-            cache.evict()
+        if api == "step":
+            outs.append(cache.step(kb[t].cuda(), vb[t].cuda(), fl, qb[t].cuda(), sc, shift=shift))
         else:
-            cache.push(kb[t].cuda(), vb[t].cuda(), fl)
+            if api == "split":
+                cache.append(kb[t].cuda(), vb[t].cuda(), fl)
+                cache.evict()
+            else:
+                cache.push(kb[t].cuda(), vb[t].cuda(), fl)
+            outs.append(cache.decode(qb[t].cuda(), sc, shift=shift))
         for b in range(B):
             sims[b].append(int(flags[t, b]))
             sims[b].evict()
-        outs.append(cache.decode(qb[t].cuda(), sc, shift=shift))
         if t < 12 or t % 7 == 0 or t == T - 1:
             torch.cuda.synchronize()
             _check_state(cache, sims, kb, vb, t)
@@ -83,7 +93,7 @@ def test_cache_steps_against_simulator(case):
     ref, _ = orc.decode_run(as_f64(qb), as_f64(kb), as_f64(vb), flags, a, s, n, wl.theta, shift, sc)
     for t in range(T):
         assert max_abs(as_f64(outs[t]), ref[t]) <= TOL_BF16, t
-    assert int(cache.state[:, 6].abs().sum().cpu()) == 0  # no overflow flag
+    assert int(cache.state[..., 6].abs().sum().cpu()) == 0  # no overflow flag
 
 
 def test_llama_decode_full_run_sampled():
@@ -99,14 +109,16 @@ def test_llama_decode_full_run_sampled():
     sc = 1 / math.sqrt(wl.d)
     outs = {}
     for t in range(wl.T):
-        cache.push(kd[t], vd[t], fd[t])
+        if t in sample:
+            outs[t] = cache.step(kd[t], vd[t], fd[t], qb[sample.index(t)].cuda(), sc, shift=True)
+        else:
+            cache.push(kd[t], vd[t], fd[t])
         for b in range(wl.B):
             sims[b].append(int(flags[t, b]))
             sims[b].evict()
         if t in sample:
-            outs[t] = cache.decode(qb[sample.index(t)].cuda(), sc, shift=True)
-            torch.cuda.synchronize()
             if t in (0, 5, 261, 793, 4095, 8191):
+                torch.cuda.synchronize()
                 _check_state(cache, sims, kb, vb, t)
     torch.cuda.synchronize()
     assert all(len(s.order()) == wl.a + wl.s + wl.n for s in sims)
@@ -128,8 +140,7 @@ def test_cache_resume_and_determinism():
     def run(cache, t0, t1):
         out = []
         for t in range(t0, t1):
-            cache.push(kd[t], vd[t], fd[t])
-            out.append(cache.decode(qb[t]))
+            out.append(cache.step(kd[t], vd[t], fd[t], qb[t]))
         return out
 
     c1 = sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta)
@@ -157,5 +168,5 @@ def test_append_without_evict_sets_overflow_flag():
     cache.append(k, k, f)
     torch.cuda.synchronize()
     st = cache.state.cpu().numpy()
-    assert np.all(st[:, 6] & 1)
-    assert np.all(st[:, 0] == 4)  # the last token was not taken
+    assert np.all(st[..., 6] & 1)
+    assert np.all(st[..., 0] == 4)  # the last token was not taken
