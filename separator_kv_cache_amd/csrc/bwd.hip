@@ -487,7 +487,7 @@ int sepattn_launch_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
   p.B = s->B; p.Hq = s->Hq; p.Hkv = s->Hkv; p.L = s->L; p.a = m->a; p.n = m->n;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
-  const int rows = fwd_tile_rows(m->n);
+  const int rows = m->n <= 256 ? 64 : 128;  // dQ query tile (its own traversal)
   p.n_qtiles = (s->L + rows - 1) / rows;
   p.n_key_tiles = (s->L + 127) / 128;
   int rc;

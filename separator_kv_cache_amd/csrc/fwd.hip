@@ -17,6 +17,7 @@
 namespace {
 
 constexpr int BK = 64;  // keys per tile
+constexpr float RESCALE_SLACK = 8.f;  // log2 units
 
 template <typename T, int D>
 struct FwdLayout;
@@ -199,7 +200,11 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
       }
     }
 
-    // ---- scale, mask, online softmax (log2 domain)
+    // ---- mask, online softmax (log2 domain).  The running reference max m_run
+    // is raised only when some lane's tile max exceeds it by more than
+    // RESCALE_SLACK (a wave-uniform branch), so O and l are rarely rescaled;
+    // probabilities stay below 2^RESCALE_SLACK.  O / l and the LSE use the
+    // same reference, so the result does not depend on when it moved.
     bool full;
     int k0 = 0;
     if (t < n_gt) {
@@ -208,13 +213,11 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
       k0 = tk.band_lo + (t - n_gt) * BK;
       full = (k0 + BK <= tk.band_hi) && (k0 + BK - 1 <= r0) && (r0 + 31 - k0 < p.n);
     }
-    float mx = -INFINITY;
+    if (!full) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < NKB; ++kb2) {
+      for (int kb2 = 0; kb2 < NKB; ++kb2) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = sacc[kb2][r] * p.scale_log2;
-        if (!full) {
+        for (int r = 0; r < 16; ++r) {
           const int kl = kb2 * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
           bool keep;
           if (t < n_gt) keep = t * BK + kl < tk.n_gather;
@@ -222,32 +225,36 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
             const int j = k0 + kl;
             keep = j < tk.band_hi && band_keep(my_row, j, p.a, p.n, fs);
           }
-          x = keep ? x : -INFINITY;
+          if (!keep) sacc[kb2][r] = -INFINITY;
         }
-        sacc[kb2][r] = x;
-        mx = fmaxf(mx, x);
       }
     }
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float ls = 0.f;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb2][r]);
+    mx = fmaxf(mx, xor32(mx)) * p.scale_log2;  // the scale is positive
+    if (__any(mx > m_run + RESCALE_SLACK)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; ++kb2) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(sacc[kb2][r] - m_use);
+        const float e = fast_exp2(__builtin_fmaf(sacc[kb2][r], p.scale_log2, -m_use));
         sacc[kb2][r] = e;
-        ls += e;
+        l_run += e;
       }
     }
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
 
     // ---- O^T += V^T P^T
     if constexpr (BF) {
@@ -340,11 +347,11 @@ int sepattn_launch_fwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
   p.scale_log2 = scale * 1.4426950408889634f;
   const int rows = fwd_tile_rows(m->n);
   p.n_qtiles = (s->L + rows - 1) / rows;
-  const bool four = rows == 128;
+  const bool big = rows == 256;
   if (dtype == SEPATTN_BF16) {
-    if (s->d == 128) return four ? launch_fwd<bf16, 128, 4>(p, st) : launch_fwd<bf16, 128, 2>(p, st);
-    return four ? launch_fwd<bf16, 64, 4>(p, st) : launch_fwd<bf16, 64, 2>(p, st);
+    if (s->d == 128) return big ? launch_fwd<bf16, 128, 8>(p, st) : launch_fwd<bf16, 128, 2>(p, st);
+    return big ? launch_fwd<bf16, 64, 8>(p, st) : launch_fwd<bf16, 64, 2>(p, st);
   }
-  if (s->d == 128) return four ? launch_fwd<float, 128, 4>(p, st) : launch_fwd<float, 128, 2>(p, st);
-  return four ? launch_fwd<float, 64, 4>(p, st) : launch_fwd<float, 64, 2>(p, st);
+  if (s->d == 128) return big ? launch_fwd<float, 128, 8>(p, st) : launch_fwd<float, 128, 2>(p, st);
+  return big ? launch_fwd<float, 64, 8>(p, st) : launch_fwd<float, 64, 2>(p, st);
 }

@@ -40,6 +40,7 @@ __device__ __forceinline__ bool band_keep(int i, int j, int a, int n, const uint
   return j <= i && (j < a || i - j < n || is_sep_b[j] != 0);
 }
 
-// Rows per query tile of the forward (and of the dQ pass), chosen from the
-// window only so that the mask expansion can reproduce the same tiling.
-static inline int fwd_tile_rows(int n) { return n <= 256 ? 64 : 128; }
+// Rows per query tile of the forward, chosen from the window only so that the
+// mask expansion can reproduce the same tiling: short windows take small
+// tiles (less band waste), long ones 256 rows (8 waves sharing each K/V tile).
+static inline int fwd_tile_rows(int n) { return n <= 256 ? 64 : 256; }
