@@ -114,6 +114,9 @@ SEPATTN_API int sepattn_mask_bits(const sepattn_mask* m, uint32_t* bits, void* s
  *
  * Q, O, dO, dQ: [B, Hq, L, d]; K, V, dK, dV: [B, Hkv, L, d], addressed with
  * element strides (batch, head, token) and a contiguous last dimension.
+ * Strides are multiples of 16 bytes, and the rows of one (sequence, head)
+ * slice span less than 2 GiB ((L - 1) * token stride + d elements), else
+ * SEPATTN_ENOTSUP: the kernels address a slice with 32-bit offsets.
  * q head h reads KV head h / (Hq / Hkv).  Inputs already carry their
  * positional encoding (plain RoPE for training-length inputs, [HUB] A1).
  * ------------------------------------------------------------------------ */

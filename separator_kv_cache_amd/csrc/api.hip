@@ -148,6 +148,12 @@ static int check_shape(const sepattn_shape* s, int dtype, const sepattn_mask* m,
       if ((st[t][i] * esz) % 16 != 0)
         return sepattn_fail(SEPATTN_EINVAL, "%s: strides must be multiples of 16 bytes", who);
     }
+  for (int t = 0; t < 4; ++t) {
+    const int64_t span = (((int64_t)s->L - 1) * st[t][2] + s->d) * esz;
+    if (span >= ((int64_t)1 << 31))
+      return sepattn_fail(SEPATTN_ENOTSUP, "%s: a (sequence, head) slice spans %lld bytes (limit 2 GiB)", who,
+                          (long long)span);
+  }
   return SEPATTN_OK;
 }
 

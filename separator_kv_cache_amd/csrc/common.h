@@ -62,6 +62,29 @@ __device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }
 
+// Raw buffer loads.  A resource covers `bytes` bytes from `base`; a load at an
+// offset past the end returns zeros without touching memory, so absent rows
+// need no branch.  Offsets are 32-bit, which bounds one resource to 2 GiB.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t BUF_OOB = 0x80000000u;  // an offset past the end of every resource
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  // dword 3 = 0x00020000: 32-bit data format, the value raw buffer loads need on gfx9-family parts
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ int bld4(rsrc_t r, uint32_t off) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+
+// l + a.x + a.y for two bf16 values packed in a dword (one v_dot2 instruction).
+__device__ __forceinline__ float add_bf16x2(uint32_t a, float l) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), one, l, false);
+}
+
 // Swap values between lane l and lane l ^ 32.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 

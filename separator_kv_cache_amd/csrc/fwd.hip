@@ -28,7 +28,7 @@ struct FwdLayout<bf16, D> {
   static constexpr int VSTR = D == 128 ? 160 : 96;   // V row stride: 16 (mod 64) dwords
   static constexpr int K_BYTES = BK * KSTR * 2;
   static constexpr int V_BYTES = BK * VSTR * 2;
-  static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
+  static constexpr int BUF_BYTES = K_BYTES + V_BYTES + 16;  // + separator bits of the tile
 };
 
 template <int D>
@@ -37,7 +37,7 @@ struct FwdLayout<float, D> {
   static constexpr int VSTR = D + 4;
   static constexpr int K_BYTES = BK * KSTR * 4;
   static constexpr int V_BYTES = BK * VSTR * 4;
-  static constexpr int BUF_BYTES = K_BYTES + V_BYTES;
+  static constexpr int BUF_BYTES = K_BYTES + V_BYTES + 16;  // + separator bits of the tile
 };
 
 struct FwdParams {
@@ -47,6 +47,7 @@ struct FwdParams {
   void* o;
   float* lse;
   int64_t sq[3], sk[3], sv[3], so[3];
+  uint32_t k_span, v_span;  // bytes of one (sequence, KV head) slice of K, V
   const uint8_t* is_sep;
   const int32_t* sep_idx;
   const int32_t* sep_before;
@@ -55,44 +56,45 @@ struct FwdParams {
   float scale_log2;  // softmax scale * log2(e)
 };
 
-// Loads one 64-key tile (rows of K and V) of the workgroup into registers.
-// Row r of the tile is key key_of(r) or absent (< 0: zeros).
+// Moves one 64-key tile (rows of K and V) of the workgroup through registers
+// into LDS.  Thread x always handles 16-byte chunk x % CH_PER_ROW of rows
+// x / CH_PER_ROW + u * ROWS_PER_PASS.  A row whose key is < 0 loads as zeros.
 template <typename T, int D, int NT>
 struct TileLoader {
   static constexpr int CH_PER_ROW = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
-  static constexpr int NCH = BK * CH_PER_ROW;
-  static constexpr int PER_THREAD = NCH / NT;
-  static_assert(NCH % NT == 0, "tile chunks must divide the workgroup");
+  static constexpr int ROWS_PER_PASS = NT / CH_PER_ROW;
+  static constexpr int PER_THREAD = BK / ROWS_PER_PASS;
+  static_assert(NT % CH_PER_ROW == 0 && BK % ROWS_PER_PASS == 0, "tile chunks must divide the workgroup");
   u32x4 kr[PER_THREAD], vr[PER_THREAD];
 
-  template <typename KeyOf>
-  __device__ __forceinline__ void load(const T* kbase, const T* vbase, int64_t skl, int64_t svl,
-                                       KeyOf key_of) {
+  __device__ static int row(int u) { return (int)threadIdx.x / CH_PER_ROW + u * ROWS_PER_PASS; }
+  __device__ static int chunk() { return (int)threadIdx.x % CH_PER_ROW; }
+
+  __device__ __forceinline__ void load(rsrc_t krs, rsrc_t vrs, uint32_t krow, uint32_t vrow,
+                                       const int (&key)[PER_THREAD]) {
+    const uint32_t c16 = chunk() * 16;
 #pragma unroll
     for (int u = 0; u < PER_THREAD; ++u) {
-      const int ch = threadIdx.x + u * NT;
-      const int r = ch / CH_PER_ROW, c = ch % CH_PER_ROW;
-      const int j = key_of(r);
-      if (j >= 0) {
-        kr[u] = ld16((const char*)(kbase + (int64_t)j * skl) + c * 16);
-        vr[u] = ld16((const char*)(vbase + (int64_t)j * svl) + c * 16);
-      } else {
-        kr[u] = u32x4{0, 0, 0, 0};
-        vr[u] = u32x4{0, 0, 0, 0};
-      }
+      const bool ok = key[u] >= 0;
+      kr[u] = bld16(krs, ok ? (uint32_t)key[u] * krow + c16 : BUF_OOB);
+      vr[u] = bld16(vrs, ok ? (uint32_t)key[u] * vrow + c16 : BUF_OOB);
     }
   }
   template <int KSTR, int VSTR>
   __device__ __forceinline__ void store(T* ks, T* vs) {
 #pragma unroll
     for (int u = 0; u < PER_THREAD; ++u) {
-      const int ch = threadIdx.x + u * NT;
-      const int r = ch / CH_PER_ROW, c = ch % CH_PER_ROW;
+      const int r = row(u), c = chunk();
       st16((char*)(ks + r * KSTR) + c * 16, kr[u]);
       st16((char*)(vs + r * VSTR) + c * 16, vr[u]);
     }
   }
 };
+
+// Bits [0, x) set, x clamped to [0, 64].
+__device__ __forceinline__ uint64_t below64(int x) {
+  return x <= 0 ? 0ull : x >= 64 ? ~0ull : ((1ull << x) - 1ull);
+}
 
 template <typename T, int D, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
@@ -142,24 +144,65 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
     }
   }
 
-  auto key_of = [&](int t, int r) -> int {
+  // ---- key schedule.  Gathered tiles take their keys from sep_idx; those
+  // indices are loaded one tile ahead of the K/V rows they address, so no
+  // load waits on another inside the loop.
+  using LD = TileLoader<T, D, NT>;
+  constexpr int PT = LD::PER_THREAD;
+  const rsrc_t krs = make_rsrc(kb, p.k_span), vrs = make_rsrc(vb, p.v_span);
+  const rsrc_t irs = make_rsrc(si, (uint32_t)p.L * 4u);
+  const uint32_t krow = (uint32_t)(p.sk[2] * sizeof(T)), vrow = (uint32_t)(p.sv[2] * sizeof(T));
+  int raw[PT], key[PT];
+  auto issue_idx = [&](int t) {  // sep_idx entries of gathered tile t
     if (t < n_gt) {
-      const int c = t * BK + r;
-      return c < tk.n_gather ? gather_key(c, tk.n_sink, si) : -1;
+#pragma unroll
+      for (int u = 0; u < PT; ++u) {
+        const int c = t * BK + LD::row(u) - tk.n_sink;
+        raw[u] = bld4(irs, c >= 0 && c < tk.n_gather - tk.n_sink ? (uint32_t)c * 4u : BUF_OOB);
+      }
     }
-    const int j = tk.band_lo + (t - n_gt) * BK + r;
-    return j < tk.band_hi ? j : -1;
+  };
+  auto keys_of = [&](int t) {  // keys of tile t (raw holds its indices if gathered)
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int r = LD::row(u);
+      if (t < n_gt) {
+        const int c = t * BK + r;
+        key[u] = c < tk.n_sink ? c : (c < tk.n_gather ? raw[u] : -1);
+      } else {
+        const int j = tk.band_lo + (t - n_gt) * BK + r;
+        key[u] = j < tk.band_hi ? j : -1;
+      }
+    }
   };
 
-  TileLoader<T, D, NT> ld;
+  // Separator flags of a band tile travel with it as a 64-bit mask (bit r =
+  // is_sep of row r), built by wave 0 with one ballot.
+  const rsrc_t frs = make_rsrc(fs, (uint32_t)p.L);
+  uint32_t flag = 0;
+  auto issue_flag = [&](int t) {
+    if (wave == 0) flag = t >= n_gt ? __builtin_amdgcn_raw_buffer_load_b8(frs, tk.band_lo + (t - n_gt) * BK + lane, 0, 0) : 0;
+  };
+
+  LD ld;
   auto kbuf = [&](int s) { return (T*)(smem + s * LY::BUF_BYTES); };
   auto vbuf = [&](int s) { return (T*)(smem + s * LY::BUF_BYTES + LY::K_BYTES); };
+  auto fbuf = [&](int s) { return (uint64_t*)(smem + s * LY::BUF_BYTES + LY::K_BYTES + LY::V_BYTES); };
+  auto store_tile = [&](int s) {
+    ld.template store<KSTR, VSTR>(kbuf(s), vbuf(s));
+    if (wave == 0) {
+      const uint64_t bits = __ballot(flag != 0);
+      if (lane == 0) *fbuf(s) = bits;
+    }
+  };
 
-  // ---- prologue: tile 0
-  if (n_tiles > 0) {
-    ld.load(kb, vb, p.sk[2], p.sv[2], [&](int r) { return key_of(0, r); });
-    ld.template store<KSTR, VSTR>(kbuf(0), vbuf(0));
-  }
+  // ---- prologue: tile 0 into LDS, indices of tile 1 in flight
+  issue_idx(0);
+  keys_of(0);
+  ld.load(krs, vrs, krow, vrow, key);
+  issue_flag(0);
+  issue_idx(1);
+  store_tile(0);
   __syncthreads();
 
   constexpr int NKB = BK / 32;  // 32-key blocks per tile
@@ -171,8 +214,11 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
 
   for (int t = 0; t < n_tiles; ++t) {
     const int cur = t & 1;
-    const bool more = t + 1 < n_tiles;
-    if (more) ld.load(kb, vb, p.sk[2], p.sv[2], [&](int r) { return key_of(t + 1, r); });
+    // Tile t + 1 (all-absent past the last tile: zero loads, unused store).
+    keys_of(t + 1);
+    ld.load(krs, vrs, krow, vrow, key);
+    issue_flag(t + 1);
+    issue_idx(t + 2);
     const T* ks = kbuf(cur);
     const T* vs = vbuf(cur);
 
@@ -205,28 +251,30 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
     // RESCALE_SLACK (a wave-uniform branch), so O and l are rarely rescaled;
     // probabilities stay below 2^RESCALE_SLACK.  O / l and the LSE use the
     // same reference, so the result does not depend on when it moved.
-    bool full;
-    int k0 = 0;
-    if (t < n_gt) {
-      full = (t + 1) * BK <= tk.n_gather;
-    } else {
-      k0 = tk.band_lo + (t - n_gt) * BK;
-      full = (k0 + BK <= tk.band_hi) && (k0 + BK - 1 <= r0) && (r0 + 31 - k0 < p.n);
-    }
+    // Partial tiles: bit kl of keep64 says whether key kl of the tile is kept
+    // for this lane's row.
+    const bool gathered = t < n_gt;
+    const int k0 = tk.band_lo + (t - n_gt) * BK;
+    const bool full = gathered ? (t + 1) * BK <= tk.n_gather
+                               : (k0 + BK <= tk.band_hi) && (k0 + BK - 1 <= r0) && (r0 + 31 - k0 < p.n);
     if (!full) {
+      uint64_t keep64;
+      if (gathered) {
+        keep64 = below64(tk.n_gather - t * BK);
+      } else {
+        const int d = my_row - k0;  // key kl lies d - kl rows before this row
+        const uint64_t causal = below64(min(d, tk.band_hi - 1 - k0) + 1);
+        const uint64_t window = ~below64(d - p.n + 1);
+        const uint64_t sinks = below64(p.a - k0);
+        keep64 = causal & (window | sinks | *fbuf(cur));
+      }
+      const uint64_t kl = hh ? keep64 >> 4 : keep64;
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; ++kb2) {
+        const uint32_t w = (uint32_t)(kl >> (32 * kb2));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kl = kb2 * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          bool keep;
-          if (t < n_gt) keep = t * BK + kl < tk.n_gather;
-          else {
-            const int j = k0 + kl;
-            keep = j < tk.band_hi && band_keep(my_row, j, p.a, p.n, fs);
-          }
-          if (!keep) sacc[kb2][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (!((w >> (8 * (r >> 2) + (r & 3))) & 1u)) sacc[kb2][r] = -INFINITY;
       }
     }
     float mx = -INFINITY;
@@ -247,16 +295,12 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-    for (int kb2 = 0; kb2 < NKB; ++kb2) {
+    for (int kb2 = 0; kb2 < NKB; ++kb2)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = fast_exp2(__builtin_fmaf(sacc[kb2][r], p.scale_log2, -m_use));
-        sacc[kb2][r] = e;
-        l_run += e;
-      }
-    }
+      for (int r = 0; r < 16; ++r) sacc[kb2][r] = fast_exp2(__builtin_fmaf(sacc[kb2][r], p.scale_log2, -m_use));
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T.  In bf16, l sums the rounded probabilities that the
+    // product uses, so each row of O stays a convex combination of V rows.
     if constexpr (BF) {
       const int g = lane >> 4, li = lane & 15;
 #pragma unroll
@@ -264,6 +308,9 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
         bf16x8 pb;
 #pragma unroll
         for (int s = 0; s < 8; ++s) pb[s] = (bf16)sacc[c >> 1][(c & 1) * 8 + s];
+        const u32x4 pw = __builtin_bit_cast(u32x4, pb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l_run = add_bf16x2(pw[i], l_run);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           // lane li of group g reads V[key_base + li/4][dim_base + 4*(li%4)]
@@ -281,6 +328,7 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
         const int kb2 = c >> 4, rr = c & 15;
         const int key = kb2 * 32 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
         const float pb = sacc[kb2][rr];
+        l_run += pb;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const float a = vs[key * VSTR + db * 32 + qn];
@@ -289,7 +337,7 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
       }
     }
 
-    if (more) ld.template store<KSTR, VSTR>(kbuf(cur ^ 1), vbuf(cur ^ 1));
+    store_tile(cur ^ 1);
     __syncthreads();
   }
 
@@ -342,6 +390,9 @@ int sepattn_launch_fwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
   for (int i = 0; i < 3; ++i) {
     p.sq[i] = s->q_stride[i]; p.sk[i] = s->k_stride[i]; p.sv[i] = s->v_stride[i]; p.so[i] = s->o_stride[i];
   }
+  const int esz = dtype == SEPATTN_BF16 ? 2 : 4;
+  p.k_span = (uint32_t)((((int64_t)s->L - 1) * s->k_stride[2] + s->d) * esz);
+  p.v_span = (uint32_t)((((int64_t)s->L - 1) * s->v_stride[2] + s->d) * esz);
   p.is_sep = m->is_sep; p.sep_idx = m->sep_idx; p.sep_before = m->sep_before;
   p.B = s->B; p.Hq = s->Hq; p.Hkv = s->Hkv; p.L = s->L; p.a = m->a; p.n = m->n;
   p.scale_log2 = scale * 1.4426950408889634f;
