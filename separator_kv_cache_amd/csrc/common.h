@@ -78,15 +78,32 @@ __device__ __forceinline__ int bld4(rsrc_t r, uint32_t off) {
   return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
 
-// l + a.x + a.y for two bf16 values packed in a dword (one v_dot2 instruction).
-__device__ __forceinline__ float add_bf16x2(uint32_t a, float l) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), one, l, false);
+// Sum of the 16 elements of v as a balanced tree (short dependency chains).
+// Plain adds on purpose: v_dot2 against a ones vector would take half the
+// instructions, but on gfx950 it issues through the matrix pipe and then
+// waits behind the MFMAs of the other wave on the SIMD.
+__device__ __forceinline__ float tree_sum16(const f32x16& v) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = v[2 * i] + v[2 * i + 1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = a[2 * i] + a[2 * i + 1];
+  return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
 // Swap values between lane l and lane l ^ 32.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// max(x[l], x[l ^ 32]) without an LDS round trip.  v_permlane32_swap swaps the
+// upper 32 lanes of its first register with the lower 32 lanes of its second,
+// so on two copies of x every lane ends up holding x[l] in one and x[l ^ 32] in
+// the other.  The s_nops give the VALU-write -> permlane and permlane -> VALU
+// wait states.
+__device__ __forceinline__ float max_xor32(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -44,3 +44,26 @@ __device__ __forceinline__ bool band_keep(int i, int j, int a, int n, const uint
 // mask expansion can reproduce the same tiling: short windows take small
 // tiles (less band waste), long ones 256 rows (8 waves sharing each K/V tile).
 static inline int fwd_tile_rows(int n) { return n <= 256 ? 64 : 256; }
+
+// Workgroup order of a 1-D grid of N = B * Hq * n_qtiles query tiles.  The
+// dispatcher hands consecutive workgroups to the chip's 8 XCDs in turn, and
+// each XCD has its own L2.  Workgroup i takes logical index
+// (i % 8) * (N / 8) + i / 8, so each XCD walks one contiguous range of the
+// logical order; in that order the query heads that share a KV head are
+// adjacent and on the same query tile, heaviest tile first, so the K/V tiles
+// they stream are fetched into one L2 and reused there.
+struct TileWork {
+  int b, h, qt;
+};
+__device__ __forceinline__ TileWork tile_work(int i, int N, int Hq, int Hkv, int n_qtiles) {
+  constexpr int XCD = 8;
+  const int lam = (N % XCD == 0) ? (i % XCD) * (N / XCD) + i / XCD : i;
+  const int g = Hq / Hkv;
+  const int per = n_qtiles * g;  // workgroups per (sequence, KV head)
+  const int bk = lam / per, rem = lam % per;
+  TileWork w;
+  w.b = bk / Hkv;
+  w.h = (bk % Hkv) * g + rem % g;
+  w.qt = n_qtiles - 1 - rem / g;
+  return w;
+}
