@@ -18,7 +18,7 @@
 
 namespace {
 
-constexpr int BK = 64;   // keys per tile (dq)
+constexpr int BK = KTILE;  // keys per tile (dq)
 constexpr int RB = 64;   // rows per block (dkdv)
 
 struct BwdParams {
@@ -27,6 +27,7 @@ struct BwdParams {
   bf16 *dq, *dk, *dv;
   float* dsum;  // D [B, Hq, L]
   int64_t sq[3], sk[3], sv[3], so[3];
+  uint32_t k_span, v_span;  // bytes of one (sequence, KV head) slice of K, V
   const uint8_t* is_sep;
   const int32_t* sep_idx;
   const int32_t* sep_before;
@@ -40,44 +41,19 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------- dq
+//
+// The forward's lockstep traversal (traverse.h): every wave loads its share
+// of key tile t+1 into registers while tile t is computed from LDS.  Wave w
+// owns query rows [q0 + 32w, q0 + 32w + 32); per tile it forms S^T = K Q^T
+// and dP^T = V dO^T (one query per lane), dS^T = P^T (dP^T - D) with
+// P = exp2(scale_log2 S - lse2), then dQ^T += K^T dS^T with K^T from
+// transposing LDS reads.
 
 template <int D>
 struct DqLayout {
   static constexpr int STR = D + 8;
   static constexpr int K_BYTES = BK * STR * 2;
-  static constexpr int BUF_BYTES = 2 * K_BYTES;  // K then V
-};
-
-template <int D, int NT>
-struct KVLoader {
-  static constexpr int CH = D / 8;  // 16-byte chunks per row
-  static constexpr int PER = BK * CH / NT;
-  u32x4 kr[PER], vr[PER];
-  template <typename KeyOf>
-  __device__ __forceinline__ void load(const bf16* kb, const bf16* vb, int64_t skl, int64_t svl, KeyOf key_of) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int ch = threadIdx.x + u * NT;
-      const int r = ch / CH, c = ch % CH;
-      const int j = key_of(r);
-      if (j >= 0) {
-        kr[u] = ld16(kb + (int64_t)j * skl + c * 8);
-        vr[u] = ld16(vb + (int64_t)j * svl + c * 8);
-      } else {
-        kr[u] = u32x4{0, 0, 0, 0};
-        vr[u] = u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16* ks, bf16* vs, int str) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int ch = threadIdx.x + u * NT;
-      const int r = ch / CH, c = ch % CH;
-      st16(ks + r * str + c * 8, kr[u]);
-      st16(vs + r * str + c * 8, vr[u]);
-    }
-  }
+  static constexpr int BUF_BYTES = 2 * K_BYTES + 16;  // K, V, separator bits
 };
 
 template <int D, int WAVES>
@@ -88,9 +64,10 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.x / p.Hq, h = blockIdx.x % p.Hq;
+  const TileWork tw = tile_work(blockIdx.x, p.B * p.Hq * p.n_qtiles, p.Hq, p.Hkv, p.n_qtiles);
+  const int b = tw.b, h = tw.h;
   const int kvh = h / (p.Hq / p.Hkv);
-  const int q0 = (p.n_qtiles - 1 - (int)blockIdx.y) * BQ;
+  const int q0 = tw.qt * BQ;
   const int r0 = q0 + wave * 32;
   const int qn = lane & 31, hh = lane >> 5;
   const int my_row = r0 + qn;
@@ -98,11 +75,6 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
 
   const bf16* kb = p.k + b * p.sk[0] + kvh * p.sk[1];
   const bf16* vb = p.v + b * p.sv[0] + kvh * p.sv[1];
-  const uint8_t* fs = p.is_sep + (size_t)b * p.L;
-  const int32_t* si = p.sep_idx + (size_t)b * p.L;
-  const TileKeys tk = tile_keys(q0, BQ, p.L, p.a, p.n, p.sep_before + (size_t)b * (p.L + 1));
-  const int n_gt = (tk.n_gather + BK - 1) / BK;
-  const int n_tiles = n_gt + (tk.band_hi - tk.band_lo + BK - 1) / BK;
 
   // ---- prologue: Q, dO (B operands), LSE, D = rowsum(dO * O)
   bf16x8 qreg[NKK], doreg[NKK];
@@ -130,33 +102,52 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
   const float lse2 = row_ok ? p.lse[rowid] * 1.4426950408889634f : 0.f;
   if (row_ok && hh == 0) p.dsum[rowid] = Dv;
 
-  auto key_of = [&](int t, int r) -> int {
-    if (t < n_gt) {
-      const int c = t * BK + r;
-      return c < tk.n_gather ? gather_key(c, tk.n_sink, si) : -1;
-    }
-    const int j = tk.band_lo + (t - n_gt) * BK + r;
-    return j < tk.band_hi ? j : -1;
-  };
-  KVLoader<D, NT> ld;
+  using MV = RowMover<bf16, D, NT>;
+  constexpr int PT = MV::PT;
+  KeyStream<PT> ks;
+  ks.init(q0, BQ, p.L, p.a, p.n, p.sep_before + (size_t)b * (p.L + 1), p.sep_idx + (size_t)b * p.L,
+          p.is_sep + (size_t)b * p.L);
+  const rsrc_t krs = make_rsrc(kb, p.k_span), vrs = make_rsrc(vb, p.v_span);
+  const uint32_t krow = (uint32_t)(p.sk[2] * 2), vrow = (uint32_t)(p.sv[2] * 2);
+  int rows[PT], key[PT];
+  MV::rows(rows);
+  MV mk, mv;
+  uint32_t flag = 0;
+
   auto kbuf = [&](int s) { return (bf16*)(smem + s * LY::BUF_BYTES); };
   auto vbuf = [&](int s) { return (bf16*)(smem + s * LY::BUF_BYTES + LY::K_BYTES); };
-  if (n_tiles > 0) {
-    ld.load(kb, vb, p.sk[2], p.sv[2], [&](int r) { return key_of(0, r); });
-    ld.store(kbuf(0), vbuf(0), STR);
-  }
+  auto fbuf = [&](int s) { return (uint64_t*)(smem + s * LY::BUF_BYTES + 2 * LY::K_BYTES); };
+  auto fetch = [&](int t) {
+    ks.keys(t, rows, key);
+    mk.load(krs, krow, key);
+    mv.load(vrs, vrow, key);
+    if (wave == 0) flag = ks.flag_byte(t, lane);
+  };
+  auto store = [&](int s) {
+    mk.template store<STR>(kbuf(s));
+    mv.template store<STR>(vbuf(s));
+    if (wave == 0) {
+      const uint64_t bits = __ballot(flag != 0);
+      if (lane == 0) *fbuf(s) = bits;
+    }
+  };
+
+  ks.issue_idx(0, rows);
+  fetch(0);
+  ks.issue_idx(1, rows);
+  store(0);
   __syncthreads();
 
   f32x16 dqacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dqacc[db] = f32x16{};
 
-  for (int t = 0; t < n_tiles; ++t) {
+  for (int t = 0; t < ks.n_tiles; ++t) {
     const int cur = t & 1;
-    const bool more = t + 1 < n_tiles;
-    if (more) ld.load(kb, vb, p.sk[2], p.sv[2], [&](int r) { return key_of(t + 1, r); });
-    const bf16* ks = kbuf(cur);
-    const bf16* vs = vbuf(cur);
+    fetch(t + 1);  // all-absent past the last tile
+    ks.issue_idx(t + 2, rows);
+    const bf16* kt = kbuf(cur);
+    const bf16* vt = vbuf(cur);
 
     f32x16 sacc[NKB], dpacc[NKB];
 #pragma unroll
@@ -165,40 +156,21 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
     for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
       for (int x = 0; x < NKB; ++x) {
-        const bf16x8 ka = *(const bf16x8*)(ks + (x * 32 + qn) * STR + kk * 16 + hh * 8);
+        const bf16x8 ka = *(const bf16x8*)(kt + (x * 32 + qn) * STR + kk * 16 + hh * 8);
         sacc[x] = mfma32x16(ka, qreg[kk], sacc[x]);
-        const bf16x8 va = *(const bf16x8*)(vs + (x * 32 + qn) * STR + kk * 16 + hh * 8);
+        const bf16x8 va = *(const bf16x8*)(vt + (x * 32 + qn) * STR + kk * 16 + hh * 8);
         dpacc[x] = mfma32x16(va, doreg[kk], dpacc[x]);
       }
     }
 
-    bool full;
-    int k0 = 0;
-    if (t < n_gt) {
-      full = (t + 1) * BK <= tk.n_gather;
-    } else {
-      k0 = tk.band_lo + (t - n_gt) * BK;
-      full = (k0 + BK <= tk.band_hi) && (k0 + BK - 1 <= r0) && (r0 + 31 - k0 < p.n);
-    }
-    // dS^T = P^T (dP^T - D), kept in sacc
+    // dS^T = P^T (dP^T - D), kept in sacc; masked keys get P = exp2(-inf) = 0
+    if (!ks.full(t, r0, p.n)) mask_scores(sacc, ks.keep64(t, my_row, p.a, p.n, *fbuf(cur)), hh, -INFINITY);
 #pragma unroll
-    for (int x = 0; x < NKB; ++x) {
+    for (int x = 0; x < NKB; ++x)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = fast_exp2(sacc[x][r] * p.scale_log2 - lse2);
-        if (!full) {
-          const int kl = x * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          bool keep;
-          if (t < n_gt) keep = t * BK + kl < tk.n_gather;
-          else {
-            const int j = k0 + kl;
-            keep = j < tk.band_hi && band_keep(my_row, j, p.a, p.n, fs);
-          }
-          pr = keep ? pr : 0.f;
-        }
-        sacc[x][r] = pr * (dpacc[x][r] - Dv);
-      }
-    }
+      for (int r = 0; r < 16; ++r)
+        sacc[x][r] = fast_exp2(__builtin_fmaf(sacc[x][r], p.scale_log2, -lse2)) * (dpacc[x][r] - Dv);
+
     // dQ^T += K^T dS^T (K^T through LDS transposing reads)
     const int g = lane >> 4, li = lane & 15;
 #pragma unroll
@@ -209,14 +181,14 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int dim = db * 32 + 16 * (g & 1) + 4 * (li & 3);
-        const int key = 16 * c + 4 * (g >> 1) + (li >> 2);
-        const bf16x4 lo = lds_read_tr16(ks + key * STR + dim);
-        const bf16x4 hi = lds_read_tr16(ks + (key + 8) * STR + dim);
+        const int kr = 16 * c + 4 * (g >> 1) + (li >> 2);
+        const bf16x4 lo = lds_read_tr16(kt + kr * STR + dim);
+        const bf16x4 hi = lds_read_tr16(kt + (kr + 8) * STR + dim);
         const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         dqacc[db] = mfma32x16(a, bsv, dqacc[db]);
       }
     }
-    if (more) ld.store(kbuf(cur ^ 1), vbuf(cur ^ 1), STR);
+    store(cur ^ 1);
     __syncthreads();
   }
 
@@ -454,7 +426,7 @@ int launch_dq(const BwdParams& p, hipStream_t st) {
   auto kern = dq_kernel<D, WAVES>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return sepattn_hip_check(e, "dq smem attribute");
-  hipLaunchKernelGGL(kern, dim3(p.B * p.Hq, p.n_qtiles), dim3(WAVES * 64), smem, st, p);
+  hipLaunchKernelGGL(kern, dim3(p.B * p.Hq * p.n_qtiles), dim3(WAVES * 64), smem, st, p);
   return sepattn_hip_check(hipGetLastError(), "dq launch");
 }
 
@@ -487,12 +459,14 @@ int sepattn_launch_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
   p.B = s->B; p.Hq = s->Hq; p.Hkv = s->Hkv; p.L = s->L; p.a = m->a; p.n = m->n;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
-  const int rows = m->n <= 256 ? 64 : 128;  // dQ query tile (its own traversal)
+  p.k_span = (uint32_t)((((int64_t)s->L - 1) * s->k_stride[2] + s->d) * 2);
+  p.v_span = (uint32_t)((((int64_t)s->L - 1) * s->v_stride[2] + s->d) * 2);
+  const int rows = fwd_tile_rows(m->n);  // dQ query tile: as the forward's
   p.n_qtiles = (s->L + rows - 1) / rows;
   p.n_key_tiles = (s->L + 127) / 128;
   int rc;
-  if (s->d == 128) rc = rows == 128 ? launch_dq<128, 4>(p, st) : launch_dq<128, 2>(p, st);
-  else rc = rows == 128 ? launch_dq<64, 4>(p, st) : launch_dq<64, 2>(p, st);
+  if (s->d == 128) rc = rows == 256 ? launch_dq<128, 8>(p, st) : launch_dq<128, 2>(p, st);
+  else rc = rows == 256 ? launch_dq<64, 8>(p, st) : launch_dq<64, 2>(p, st);
   if (rc != SEPATTN_OK) return rc;
   return s->d == 128 ? launch_dkdv<128>(p, st) : launch_dkdv<64>(p, st);
 }
