@@ -19,7 +19,7 @@
 namespace {
 
 constexpr int BK = KTILE;  // keys per tile (dq)
-constexpr int RB = 64;   // rows per block (dkdv)
+constexpr int RB = 32;   // rows per block (dkdv)
 
 struct BwdParams {
   const bf16 *q, *k, *v, *o, *dout;
@@ -28,6 +28,7 @@ struct BwdParams {
   float* dsum;  // D [B, Hq, L]
   int64_t sq[3], sk[3], sv[3], so[3];
   uint32_t k_span, v_span;  // bytes of one (sequence, KV head) slice of K, V
+  uint32_t q_span, o_span;  // bytes of one (sequence, q head) slice of Q (dQ), O (dO)
   const uint8_t* is_sep;
   const int32_t* sep_idx;
   const int32_t* sep_before;
@@ -206,6 +207,17 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- dk, dv
+//
+// Key-major: a workgroup of 4 waves owns KT = 128 keys of one class and walks
+// the rows that see them in blocks of RB = 32 rows, for each q head of its KV
+// head in turn (iteration it = row block * group + head).  Wave w holds its
+// 32 keys' K and V rows as B operands and their dK^T, dV^T accumulators, so
+// it runs alone on its SIMD (over 256 registers) and overlaps its matrix and
+// vector work itself: step it forms S and dP of iteration it, then turns
+// them into P and dS while the matrix core accumulates dV^T += dO^T P and
+// dK^T += Q^T dS of iteration it - 1.  Q/dO row tiles are triple-buffered in
+// LDS: step it reads tiles it and it - 1 and writes tile it + 1 (loaded into
+// registers one step earlier) over tile it - 2.
 
 template <int D>
 struct DkvLayout {
@@ -214,62 +226,31 @@ struct DkvLayout {
   static constexpr int BUF_BYTES = 2 * T_BYTES + 2 * RB * 4;  // Q, dO, lse2, D
 };
 
-template <int D, int NT>
-struct QdoLoader {
-  static constexpr int CH = D / 8;
-  static constexpr int PER = RB * CH / NT;
-  u32x4 qr[PER], dr[PER];
-  float lse2, dsum;
-  __device__ __forceinline__ void load(const bf16* qb, const bf16* db, int64_t sql, int64_t sol,
-                                       const float* lse_row, const float* d_row, int rs, int L) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int ch = threadIdx.x + u * NT;
-      const int r = ch / CH, c = ch % CH;
-      const int i = rs + r;
-      if (i < L) {
-        qr[u] = ld16(qb + (int64_t)i * sql + c * 8);
-        dr[u] = ld16(db + (int64_t)i * sol + c * 8);
-      } else {
-        qr[u] = u32x4{0, 0, 0, 0};
-        dr[u] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (threadIdx.x < RB) {
-      const int i = rs + threadIdx.x;
-      lse2 = i < L ? lse_row[i] * 1.4426950408889634f : INFINITY;
-      dsum = i < L ? d_row[i] : 0.f;
-    }
-  }
-  __device__ __forceinline__ void store(char* buf) {
-    bf16* qs = (bf16*)buf;
-    bf16* ds = (bf16*)(buf + DkvLayout<D>::T_BYTES);
-    float* ls = (float*)(buf + 2 * DkvLayout<D>::T_BYTES);
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int ch = threadIdx.x + u * NT;
-      const int r = ch / CH, c = ch % CH;
-      st16(qs + r * DkvLayout<D>::STR + c * 8, qr[u]);
-      st16(ds + r * DkvLayout<D>::STR + c * 8, dr[u]);
-    }
-    if (threadIdx.x < RB) {
-      ls[threadIdx.x] = lse2;
-      ls[RB + threadIdx.x] = dsum;
-    }
-  }
-};
-
-template <int D, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(BwdParams p) {
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   using LY = DkvLayout<D>;
-  constexpr int NT = WAVES * 64, KT = WAVES * 32, STR = LY::STR;
+  constexpr int NT = 256, KT = 128, STR = LY::STR;
   constexpr int NDB = D / 32, NKK = D / 16;
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int PT = RB * CH / NT;       // chunks per thread per tile
+  constexpr int QB = RB / 32;             // 32-row blocks per iteration
+  constexpr int NS = 2 * NKK * QB;        // S and dP MFMAs per iteration
+  constexpr int NC = (RB / 16) * NDB * 2;  // dV and dK MFMAs per iteration
+  constexpr int NE = 16 * QB;             // P/dS elements per lane per iteration
+  constexpr int EPM = NE / NC;            // ... per dV/dK MFMA
+  static_assert(EPM * NC == NE, "P/dS elements must spread evenly over the dV/dK MFMAs");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int b = blockIdx.x / p.Hkv, kvh = blockIdx.x % p.Hkv;
-  const bool anchors = (int)blockIdx.y < p.n_key_tiles;
-  const int tile = anchors ? blockIdx.y : blockIdx.y - p.n_key_tiles;
+  // XCD-aware order (as tile_work): the key tiles of one (sequence, KV head)
+  // run on one XCD, anchor tiles (the longest row ranges) first.
+  const int per = 2 * p.n_key_tiles;
+  const int N = p.B * p.Hkv * per;
+  const int lam = (N % 8 == 0) ? ((int)blockIdx.x % 8) * (N / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
+  const int bk = lam / per, rem = lam % per;
+  const int b = bk / p.Hkv, kvh = bk % p.Hkv;
+  const bool anchors = rem < p.n_key_tiles;
+  const int tile = anchors ? rem : rem - p.n_key_tiles;
   const int n_sink = min(p.a, p.L);
   const int count = anchors ? n_sink + p.sep_cnt[b] : p.plain_cnt[b];
   const int c0 = tile * KT;
@@ -307,99 +288,208 @@ __global__ __launch_bounds__(WAVES * 64) void dkdv_kernel(BwdParams p) {
   const int group = p.Hq / p.Hkv;
   const int n_rb = (row_end - j_first + RB - 1) / RB;
   const int n_it = n_rb * group;
-  QdoLoader<D, NT> ld;
-  auto load_it = [&](int it) {
+
+  // ---- Q/dO row tiles: global -> registers -> LDS.  Thread x moves chunk
+  // x % CH of rows x / CH + u * (NT / CH); rows past L load as zeros and get
+  // lse2 = +inf, so their P is exactly 0.
+  // Byte offset of the LDS buffer of tile it (it >= 0; unsigned arithmetic
+  // lets the compiler fold constant offsets into the LDS instructions).
+  auto tbuf = [&](int it) -> uint32_t { return ((uint32_t)it % 3u) * (uint32_t)LY::BUF_BYTES; };
+  // Staging registers of one tile on its way to LDS.
+  struct Stage {
+    u32x4 q[PT], d[PT];
+    float lse, dsum;
+  };
+  auto fetch = [&](Stage& sg, int it) {
     const int rs = j_first + (it / group) * RB;
     const int h = kvh * group + it % group;
-    const bf16* qb = p.q + b * p.sq[0] + h * p.sq[1];
-    const bf16* dob = p.dout + b * p.so[0] + h * p.so[1];
-    const size_t rowb = ((size_t)b * p.Hq + h) * p.L;
-    ld.load(qb, dob, p.sq[2], p.so[2], p.lse + rowb, p.dsum + rowb, rs, p.L);
+    const bool live = it < n_it;
+    const rsrc_t qrs = make_rsrc(p.q + b * p.sq[0] + h * p.sq[1], p.q_span);
+    const rsrc_t drs = make_rsrc(p.dout + b * p.so[0] + h * p.so[1], p.o_span);
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int i = rs + (int)threadIdx.x / CH + u * (NT / CH);
+      const bool ok = live && i < p.L;
+      const uint32_t c16 = ((int)threadIdx.x % CH) * 16;
+      sg.q[u] = bld16(qrs, ok ? (uint32_t)i * (uint32_t)(p.sq[2] * 2) + c16 : BUF_OOB);
+      sg.d[u] = bld16(drs, ok ? (uint32_t)i * (uint32_t)(p.so[2] * 2) + c16 : BUF_OOB);
+    }
+    if (threadIdx.x < RB) {
+      const size_t rowb = ((size_t)b * p.Hq + h) * p.L;
+      const rsrc_t lrs = make_rsrc(p.lse + rowb, (uint32_t)p.L * 4u);
+      const rsrc_t srs = make_rsrc(p.dsum + rowb, (uint32_t)p.L * 4u);
+      const int i = rs + (int)threadIdx.x;
+      const uint32_t off = live && i < p.L ? (uint32_t)i * 4u : BUF_OOB;
+      sg.lse = __builtin_bit_cast(float, bld4(lrs, off));
+      sg.dsum = __builtin_bit_cast(float, bld4(srs, off));
+    }
   };
-  if (n_it > 0) {
-    load_it(0);
-    ld.store(smem);
-  }
-  __syncthreads();
+  auto store = [&](const Stage& sg, int it) {
+    char* buf = smem + tbuf(it);
+    bf16* qs = (bf16*)buf;
+    bf16* ds = (bf16*)(buf + LY::T_BYTES);
+    float* ls = (float*)(buf + 2 * LY::T_BYTES);
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int r = (int)threadIdx.x / CH + u * (NT / CH), c = (int)threadIdx.x % CH;
+      st16(qs + r * STR + c * 8, sg.q[u]);
+      st16(ds + r * STR + c * 8, sg.d[u]);
+    }
+    if (threadIdx.x < RB) {
+      const int rs = j_first + (it / group) * RB;
+      const bool ok = rs + (int)threadIdx.x < p.L;
+      ls[threadIdx.x] = ok ? sg.lse * 1.4426950408889634f : INFINITY;
+      ls[RB + threadIdx.x] = ok ? sg.dsum : 0.f;
+    }
+  };
 
   f32x16 dkacc[NDB], dvacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) { dkacc[db] = f32x16{}; dvacc[db] = f32x16{}; }
+  const int g = lane >> 4, li = lane & 15;
 
-  for (int it = 0; it < n_it; ++it) {
-    const int cur = it & 1;
-    const bool more = it + 1 < n_it;
-    if (more) load_it(it + 1);
-    const char* buf = smem + cur * LY::BUF_BYTES;
-    const bf16* qs = (const bf16*)buf;
-    const bf16* ds = (const bf16*)(buf + LY::T_BYTES);
-    const float* ls = (const float*)(buf + 2 * LY::T_BYTES);
+  // S = Q K^T and dP = dO V^T of iteration it: RB rows x this wave's 32 keys
+  // (lane = key) into s[0..QB) (S) and s[QB..2QB) (dP); operand reads PD ahead.
+  f32x16 s[2 * QB];
+  auto sdp = [&](int it) {
+    const char* base = smem + tbuf(it) + (qn * STR + hh * 8) * 2;
+    // MFMA i: S (i even) or dP (i odd), so that consecutive MFMAs never
+    // accumulate into the same registers; kk = i / (2 QB), qb = (i / 2) % QB
+    auto opnd = [&](int i) -> bf16x8 {
+      const int kk = i / (2 * QB), qb = (i / 2) % QB;
+      const int off = ((i & 1) ? LY::T_BYTES : 0) + (qb * 32 * STR + kk * 16) * 2;  // Q for S, dO for dP
+      return *(const bf16x8*)(base + off);
+    };
+    constexpr int PD = 4;
+    bf16x8 op[NS];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) op[i] = opnd(i);
+#pragma unroll
+    for (int x = 0; x < 2 * QB; ++x) s[x] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (i + PD < NS) op[i + PD] = opnd(i + PD);
+      const int kk = i / (2 * QB), qb = (i / 2) % QB;
+      if (i & 1) s[QB + qb] = mfma32x16(op[i], vreg[kk], s[QB + qb]);
+      else s[qb] = mfma32x16(op[i], kreg[kk], s[qb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // P, dS of iteration it (element e of this lane's NE) from s and the rows'
+  // lse2, D, as the B operands of the row contraction: chunk c holds rows
+  // 16c .. 16c + 15, slot sl is register (c & 1) * 8 + sl of block c >> 1.
+  // This lane's key is seen by the local rows [lo, hi) of the block (its
+  // position, the end of the sequence and, for plain keys, the window), so
+  // the mask is two compares per element and no branch.
+  struct PdS {
+    bf16x8 p[RB / 16], d[RB / 16];
+  };
+  const int key_hi = !key_ok ? -1 : anchors ? p.L : min(p.L, my_key + p.n);  // rows [my_key, key_hi)
+  auto pds = [&](PdS& o, const float* ls, int lo, int hi, int e, bool masked) {
+    const int qb = e / 16, r = e % 16;
+    const int rl0 = qb * 32 + 8 * (r >> 2) + (r & 3);  // local row is rl0 + 4 * hh
+    const int rl = rl0 + 4 * hh;
+    float pr = fast_exp2(__builtin_fmaf(s[qb][r], p.scale_log2, -ls[rl]));
+    if (masked) pr = (rl0 >= lo && rl0 < hi) ? pr : 0.f;
+    const float dsv = pr * (s[QB + qb][r] - ls[RB + rl]);
+    const int c = qb * 2 + (r >> 3), sl = r & 7;
+    o.p[c][sl] = (bf16)pr;
+    o.d[c][sl] = (bf16)dsv;
+    if (sl & 1) {
+      // Pin the finished pair here: without a use at this point the compiler
+      // sinks the whole P/dS computation to the end of the step (its first
+      // real use is the next step's MFMAs), out of reach of the interleave.
+      const uint32_t pw = __builtin_bit_cast(u32x4, o.p[c])[sl >> 1];
+      const uint32_t dw = __builtin_bit_cast(u32x4, o.d[c])[sl >> 1];
+      asm volatile("" ::"v"(pw), "v"(dw));
+    }
+  };
+  auto pds_range = [&](int it, int& lo, int& hi) {  // in units of rl0 (hh folded in)
     const int rs = j_first + (it / group) * RB;
+    lo = my_key - rs - 4 * hh;
+    hi = key_hi - rs - 4 * hh;
+  };
 
-    // S = Q K^T and dP = dO V^T for 64 rows x 32 keys: lane = key
-    f32x16 sacc[2], dpacc[2];
+  // dV^T += dO^T P and dK^T += Q^T dS for iteration it - 1 (transposing
+  // reads of its tile, P/dS in prev), interleaved with the P/dS of iteration
+  // it into cur (EPM elements per MFMA).  Past the last iteration the P/dS
+  // are formed from stale registers and never used.
+  auto dvdk_pds = [&](int it, const PdS& prev, PdS& cur) {
+    const char* pbuf = smem + tbuf(it + 2);  // tile it - 1
+    const float* ls = (const float*)(smem + tbuf(it) + 2 * LY::T_BYTES);
+    int lo, hi;
+    pds_range(it, lo, hi);
+    // lane li of group g reads row 16c + 4(g/2) + li/4 (and that + 8) at
+    // dims db*32 + 16(g%2) + 4(li%4): a per-lane base plus constant offsets
+    const char* base = pbuf + ((4 * (g >> 1) + (li >> 2)) * STR + 16 * (g & 1) + 4 * (li & 3)) * 2;
+    auto opnd = [&](int i) -> bf16x8 {
+      const int c = i / (2 * NDB), db = (i / 2) % NDB;
+      const int off = ((i & 1) ? 0 : LY::T_BYTES) + (16 * c * STR + db * 32) * 2;  // Q for dK, dO for dV
+      const bf16x4 lo4 = lds_read_tr16(base + off);
+      const bf16x4 hi4 = lds_read_tr16(base + off + 8 * STR * 2);
+      return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    };
+    auto run = [&](bool masked) {
+      constexpr int PD = 4;
+      bf16x8 op[NC];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) { sacc[qb] = f32x16{}; dpacc[qb] = f32x16{}; }
+      for (int i = 0; i < PD; ++i) op[i] = opnd(i);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
+      for (int i = 0; i < NC; ++i) {
+        if (i + PD < NC) op[i + PD] = opnd(i + PD);
+        const int c = i / (2 * NDB), db = (i / 2) % NDB;
+        if (i & 1) dkacc[db] = mfma32x16(op[i], prev.d[c], dkacc[db]);
+        else dvacc[db] = mfma32x16(op[i], prev.p[c], dvacc[db]);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const bf16x8 qa = *(const bf16x8*)(qs + (qb * 32 + qn) * STR + kk * 16 + hh * 8);
-        sacc[qb] = mfma32x16(qa, kreg[kk], sacc[qb]);
-        const bf16x8 da = *(const bf16x8*)(ds + (qb * 32 + qn) * STR + kk * 16 + hh * 8);
-        dpacc[qb] = mfma32x16(da, vreg[kk], dpacc[qb]);
+        for (int e = 0; e < EPM; ++e) pds(cur, ls, lo, hi, i * EPM + e, masked);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    const bool full = wave_all && jw_hi <= rs && rs + RB - 1 < p.L &&
-                      (anchors || rs + RB - 1 - jw_lo < p.n);
+    };
+    run(true);
+  };
+
+  // ---- prologue: tile 0 in LDS, tile 1 in registers; step 0 = S, dP and
+  // P, dS of iteration 0
+  PdS pa, pb2;
+  Stage sg;
+  fetch(sg, 0);
+  store(sg, 0);
+  fetch(sg, 1);
+  __syncthreads();
+  sdp(0);
+  {
+    const float* ls = (const float*)(smem + 2 * LY::T_BYTES);
+    int lo, hi;
+    pds_range(0, lo, hi);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int rl = qb * 32 + 8 * i4 + 4 * hh;  // local row of register 4*i4
-        const f32x4 l2 = *(const f32x4*)(ls + rl);
-        const f32x4 dd = *(const f32x4*)(ls + RB + rl);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * i4 + e;
-          float pr = fast_exp2(sacc[qb][r] * p.scale_log2 - l2[e]);
-          if (!full) {
-            const int i = rs + rl + e;
-            bool keep = key_ok && my_key <= i && i < p.L;
-            if (!anchors) keep = keep && i - my_key < p.n;
-            pr = keep ? pr : 0.f;
-          }
-          sacc[qb][r] = pr;                           // P
-          dpacc[qb][r] = pr * (dpacc[qb][r] - dd[e]);  // dS
-        }
-      }
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS (row-contraction, transposing reads)
-    const int g = lane >> 4, li = lane & 15;
-#pragma unroll
-    for (int c = 0; c < RB / 16; ++c) {
-      bf16x8 pb, sb;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        pb[s] = (bf16)sacc[c >> 1][(c & 1) * 8 + s];
-        sb[s] = (bf16)dpacc[c >> 1][(c & 1) * 8 + s];
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int dim = db * 32 + 16 * (g & 1) + 4 * (li & 3);
-        const int row = 16 * c + 4 * (g >> 1) + (li >> 2);
-        const bf16x4 dlo = lds_read_tr16(ds + row * STR + dim);
-        const bf16x4 dhi = lds_read_tr16(ds + (row + 8) * STR + dim);
-        const bf16x8 da = {dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]};
-        dvacc[db] = mfma32x16(da, pb, dvacc[db]);
-        const bf16x4 qlo = lds_read_tr16(qs + row * STR + dim);
-        const bf16x4 qhi = lds_read_tr16(qs + (row + 8) * STR + dim);
-        const bf16x8 qa = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-        dkacc[db] = mfma32x16(qa, sb, dkacc[db]);
-      }
-    }
-    if (more) ld.store(smem + (cur ^ 1) * LY::BUF_BYTES);
+    for (int e = 0; e < NE; ++e) pds(pa, ls, lo, hi, e, true);
+  }
+  store(sg, 1);
+  fetch(sg, 2);
+  __syncthreads();
+
+  // ---- step it (1 <= it < n_it): S, dP of it; P, dS of it beside dV, dK of
+  // it - 1; tile it + 1 into LDS and tile it + 2 into the staging registers.
+  // Unrolled by two so the P/dS register sets alternate without copies.
+  auto step = [&](int it, const PdS& prev, PdS& cur) {
+    sdp(it);
+    dvdk_pds(it, prev, cur);
+    store(sg, it + 1);
+    fetch(sg, it + 2);
     __syncthreads();
+  };
+  int it = 1;
+  for (; it + 1 < n_it; it += 2) {
+    step(it, pa, pb2);
+    step(it + 1, pb2, pa);
+  }
+  // (the final dV, dK step also forms P, dS of a block past the end; unused)
+  if (it < n_it) {
+    step(it, pa, pb2);
+    dvdk_pds(it + 1, pb2, pa);
+  } else {
+    dvdk_pds(it, pa, pb2);
   }
 
   if (key_ok) {
@@ -432,12 +522,11 @@ int launch_dq(const BwdParams& p, hipStream_t st) {
 
 template <int D>
 int launch_dkdv(const BwdParams& p, hipStream_t st) {
-  constexpr int WAVES = 4;
-  const int smem = 2 * DkvLayout<D>::BUF_BYTES;
-  auto kern = dkdv_kernel<D, WAVES>;
+  const int smem = 3 * DkvLayout<D>::BUF_BYTES;
+  auto kern = dkdv_kernel<D>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return sepattn_hip_check(e, "dkdv smem attribute");
-  hipLaunchKernelGGL(kern, dim3(p.B * p.Hkv, 2 * p.n_key_tiles), dim3(WAVES * 64), smem, st, p);
+  hipLaunchKernelGGL(kern, dim3(p.B * p.Hkv * 2 * p.n_key_tiles), dim3(256), smem, st, p);
   return sepattn_hip_check(hipGetLastError(), "dkdv launch");
 }
 
@@ -461,6 +550,8 @@ int sepattn_launch_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
   p.scale_log2 = scale * 1.4426950408889634f;
   p.k_span = (uint32_t)((((int64_t)s->L - 1) * s->k_stride[2] + s->d) * 2);
   p.v_span = (uint32_t)((((int64_t)s->L - 1) * s->v_stride[2] + s->d) * 2);
+  p.q_span = (uint32_t)((((int64_t)s->L - 1) * s->q_stride[2] + s->d) * 2);
+  p.o_span = (uint32_t)((((int64_t)s->L - 1) * s->o_stride[2] + s->d) * 2);
   const int rows = fwd_tile_rows(m->n);  // dQ query tile: as the forward's
   p.n_qtiles = (s->L + rows - 1) / rows;
   p.n_key_tiles = (s->L + 127) / 128;
