@@ -19,7 +19,7 @@
 namespace {
 
 constexpr int BK = KTILE;  // keys per tile (dq)
-constexpr int RB = 32;   // rows per block (dkdv)
+constexpr int RB = 64;   // rows per block (dkdv)
 
 struct BwdParams {
   const bf16 *q, *k, *v, *o, *dout;
@@ -50,9 +50,16 @@ struct BwdParams {
 // P = exp2(scale_log2 S - lse2), then dQ^T += K^T dS^T with K^T from
 // transposing LDS reads.
 
+// Row strides of tiles read both by 16-byte row reads (MFMA operands along a
+// row) and by transposing reads: an odd number of 16-byte chunks keeps the
+// row reads of 16 lanes on distinct banks, and 19 chunks (D = 128) puts the
+// four rows of a transposing read of 16 lanes on disjoint bank windows.
+template <int D>
+constexpr int dual_read_stride() { return D == 128 ? 152 : 88; }
+
 template <int D>
 struct DqLayout {
-  static constexpr int STR = D + 8;
+  static constexpr int STR = dual_read_stride<D>();
   static constexpr int K_BYTES = BK * STR * 2;
   static constexpr int BUF_BYTES = 2 * K_BYTES + 16;  // K, V, separator bits
 };
@@ -208,42 +215,55 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- dk, dv
 //
-// Key-major: a workgroup of 4 waves owns KT = 128 keys of one class and walks
-// the rows that see them in blocks of RB = 32 rows, for each q head of its KV
-// head in turn (iteration it = row block * group + head).  Wave w holds its
-// 32 keys' K and V rows as B operands and their dK^T, dV^T accumulators, so
-// it runs alone on its SIMD (over 256 registers) and overlaps its matrix and
-// vector work itself: step it forms S and dP of iteration it, then turns
-// them into P and dS while the matrix core accumulates dV^T += dO^T P and
-// dK^T += Q^T dS of iteration it - 1.  Q/dO row tiles are triple-buffered in
-// LDS: step it reads tiles it and it - 1 and writes tile it + 1 (loaded into
-// registers one step earlier) over tile it - 2.
+// Key-major: a workgroup of 8 waves owns KT = 128 keys of one class and walks
+// the rows that see them in blocks of RB = 64 rows, for each q head of its KV
+// head in turn (iteration it = row block * group + head).  Waves 2kg and
+// 2kg + 1 own the same 32 keys (key group kg).  Per block, the wave with
+// hf = w % 2 forms S = Q K^T and dP = dO V^T for the rows [32 hf, 32 hf + 32)
+// and from them P and dS, which the two waves exchange through LDS (phase
+// A); then it accumulates dV^T += dO^T P and dK^T += Q^T dS over all 64 rows
+// for the head dims [D/2 hf, D/2 hf + D/2) (phase B).  No MFMA work is
+// duplicated, and a wave keeps K, V of its keys for all dims but dK, dV for
+// half of them, which fits two waves per SIMD.
+//
+// The two waves on a SIMD (w and w + 4) belong to different key-group
+// pairs, and the second half of the workgroup runs one phase behind the
+// first (one extra barrier), so while one wave exponentiates in phase A the
+// other keeps the matrix core busy in phase B.  Every wave runs A(it),
+// barrier, B(it), barrier.  Tile it + 1 of Q/dO is written over tile it - 1
+// in the interval where the first half runs B(it) and the second half A(it)
+// (both halves store from those phases), and the loads of tile it + 2 start
+// there; tile it - 1 was last read by the second half's B(it - 1), one
+// interval earlier.
 
 template <int D>
 struct DkvLayout {
-  static constexpr int STR = D + 8;
-  static constexpr int T_BYTES = RB * STR * 2;
+  static constexpr int STR = dual_read_stride<D>();           // Q/dO row stride (elements)
+  static constexpr int T_BYTES = RB * STR * 2;                // one Q or dO tile
   static constexpr int BUF_BYTES = 2 * T_BYTES + 2 * RB * 4;  // Q, dO, lse2, D
+  static constexpr int PSTR = RB + 8;                         // P/dS: row stride per key (elements)
+  static constexpr int X_BYTES = 128 * PSTR * 2;              // P or dS of the 128 keys
+  static constexpr int SMEM = 2 * BUF_BYTES + 2 * X_BYTES;
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
   using LY = DkvLayout<D>;
-  constexpr int NT = 256, KT = 128, STR = LY::STR;
-  constexpr int NDB = D / 32, NKK = D / 16;
-  constexpr int CH = D / 8;              // 16-byte chunks per row
-  constexpr int PT = RB * CH / NT;       // chunks per thread per tile
-  constexpr int QB = RB / 32;             // 32-row blocks per iteration
-  constexpr int NS = 2 * NKK * QB;        // S and dP MFMAs per iteration
-  constexpr int NC = (RB / 16) * NDB * 2;  // dV and dK MFMAs per iteration
-  constexpr int NE = 16 * QB;             // P/dS elements per lane per iteration
-  constexpr int EPM = NE / NC;            // ... per dV/dK MFMA
-  static_assert(EPM * NC == NE, "P/dS elements must spread evenly over the dV/dK MFMAs");
+  constexpr int NT = 512, KT = 128, STR = LY::STR, PSTR = LY::PSTR;
+  constexpr int NKK = D / 16;          // 16-dim steps of S and dP
+  constexpr int HD = D / 2;            // head dims whose dK, dV a wave accumulates
+  constexpr int NDBH = HD / 32;        // 32-dim blocks of them
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int PT = RB * CH / NT;     // tile chunks per thread (Q and dO each)
+  static_assert(PT * NT == RB * CH, "tile chunks must divide the workgroup");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kg = wave >> 1, hf = wave & 1, half = wave >> 2;
   // XCD-aware order (as tile_work): the key tiles of one (sequence, KV head)
-  // run on one XCD, anchor tiles (the longest row ranges) first.
+  // run on one XCD, anchor tiles (the longest row ranges) first.  (Spreading
+  // one head over all XCDs instead, to share the Infinity Cache, measured
+  // slower and with more L2 misses.)
   const int per = 2 * p.n_key_tiles;
   const int N = p.B * p.Hkv * per;
   const int lam = (N % 8 == 0) ? ((int)blockIdx.x % 8) * (N / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
@@ -260,19 +280,14 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   auto key_at = [&](int c) -> int { return anchors ? (c < n_sink ? c : si[c - n_sink]) : pl[c]; };
 
   const int qn = lane & 31, hh = lane >> 5;
-  const int my_c = c0 + wave * 32 + qn;
+  const int my_c = c0 + kg * 32 + qn;
   const bool key_ok = my_c < count;
   const int my_key = key_ok ? key_at(my_c) : 0;
-  const int c_last = min(c0 + KT, count) - 1;
-  const int j_first = key_at(c0), j_last = key_at(c_last);
-  const int wc_last = min(c0 + wave * 32 + 31, count - 1);
-  const bool wave_any = c0 + wave * 32 < count;
-  const bool wave_all = c0 + wave * 32 + 31 < count;
-  const int jw_lo = wave_any ? key_at(c0 + wave * 32) : 0;
-  const int jw_hi = wave_any ? key_at(wc_last) : 0;
+  const int j_first = key_at(c0), j_last = key_at(min(c0 + KT, count) - 1);
   const int row_end = anchors ? p.L : min(p.L, j_last + p.n);
+  const int key_hi = !key_ok ? -1 : anchors ? p.L : min(p.L, my_key + p.n);  // rows [my_key, key_hi) see it
 
-  // ---- this wave's 32 keys as B operands (K^T, V^T rows per lane)
+  // ---- this lane's key as B operands (K^T, V^T rows), all head dims
   bf16x8 kreg[NKK], vreg[NKK];
   {
     const bf16* krow = p.k + b * p.sk[0] + kvh * p.sk[1] + (int64_t)my_key * p.sk[2];
@@ -292,211 +307,193 @@ __global__ __launch_bounds__(256) void dkdv_kernel(BwdParams p) {
   // ---- Q/dO row tiles: global -> registers -> LDS.  Thread x moves chunk
   // x % CH of rows x / CH + u * (NT / CH); rows past L load as zeros and get
   // lse2 = +inf, so their P is exactly 0.
-  // Byte offset of the LDS buffer of tile it (it >= 0; unsigned arithmetic
-  // lets the compiler fold constant offsets into the LDS instructions).
-  auto tbuf = [&](int it) -> uint32_t { return ((uint32_t)it % 3u) * (uint32_t)LY::BUF_BYTES; };
-  // Staging registers of one tile on its way to LDS.
-  struct Stage {
-    u32x4 q[PT], d[PT];
-    float lse, dsum;
-  };
-  auto fetch = [&](Stage& sg, int it) {
-    const int rs = j_first + (it / group) * RB;
-    const int h = kvh * group + it % group;
+  u32x4 qr[PT], dr[PT];
+  float lse_r = 0.f, d_r = 0.f;
+  bool lse_ok = false;
+  // fetch() is called for it = 0, 1, 2, ... in order: (row block, head) of
+  // the next call advance as counters instead of divisions.
+  int f_rs = j_first, f_h = kvh * group;
+  auto fetch = [&](int it) {
+    // (uniform values; readfirstlane keeps the buffer resources in scalar
+    // registers, else each load becomes a loop over distinct descriptors)
+    const int rs = __builtin_amdgcn_readfirstlane(f_rs), h = __builtin_amdgcn_readfirstlane(f_h);
     const bool live = it < n_it;
+    if (++f_h == (kvh + 1) * group) { f_h = kvh * group; f_rs += RB; }
     const rsrc_t qrs = make_rsrc(p.q + b * p.sq[0] + h * p.sq[1], p.q_span);
     const rsrc_t drs = make_rsrc(p.dout + b * p.so[0] + h * p.so[1], p.o_span);
+    const uint32_t qrow = (uint32_t)(p.sq[2] * 2), orow = (uint32_t)(p.so[2] * 2);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int i = rs + (int)threadIdx.x / CH + u * (NT / CH);
       const bool ok = live && i < p.L;
       const uint32_t c16 = ((int)threadIdx.x % CH) * 16;
-      sg.q[u] = bld16(qrs, ok ? (uint32_t)i * (uint32_t)(p.sq[2] * 2) + c16 : BUF_OOB);
-      sg.d[u] = bld16(drs, ok ? (uint32_t)i * (uint32_t)(p.so[2] * 2) + c16 : BUF_OOB);
+      qr[u] = bld16(qrs, ok ? (uint32_t)i * qrow + c16 : BUF_OOB);
+      dr[u] = bld16(drs, ok ? (uint32_t)i * orow + c16 : BUF_OOB);
     }
     if (threadIdx.x < RB) {
       const size_t rowb = ((size_t)b * p.Hq + h) * p.L;
       const rsrc_t lrs = make_rsrc(p.lse + rowb, (uint32_t)p.L * 4u);
       const rsrc_t srs = make_rsrc(p.dsum + rowb, (uint32_t)p.L * 4u);
       const int i = rs + (int)threadIdx.x;
-      const uint32_t off = live && i < p.L ? (uint32_t)i * 4u : BUF_OOB;
-      sg.lse = __builtin_bit_cast(float, bld4(lrs, off));
-      sg.dsum = __builtin_bit_cast(float, bld4(srs, off));
+      lse_ok = live && i < p.L;
+      const uint32_t off = lse_ok ? (uint32_t)i * 4u : BUF_OOB;
+      lse_r = __builtin_bit_cast(float, bld4(lrs, off));
+      d_r = __builtin_bit_cast(float, bld4(srs, off));
     }
   };
-  auto store = [&](const Stage& sg, int it) {
+  auto tbuf = [&](int it) -> uint32_t { return ((uint32_t)it & 1u) * (uint32_t)LY::BUF_BYTES; };
+  auto store = [&](int it) {
     char* buf = smem + tbuf(it);
-    bf16* qs = (bf16*)buf;
-    bf16* ds = (bf16*)(buf + LY::T_BYTES);
-    float* ls = (float*)(buf + 2 * LY::T_BYTES);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int r = (int)threadIdx.x / CH + u * (NT / CH), c = (int)threadIdx.x % CH;
-      st16(qs + r * STR + c * 8, sg.q[u]);
-      st16(ds + r * STR + c * 8, sg.d[u]);
+      st16(buf + (r * STR + c * 8) * 2, qr[u]);
+      st16(buf + LY::T_BYTES + (r * STR + c * 8) * 2, dr[u]);
     }
     if (threadIdx.x < RB) {
-      const int rs = j_first + (it / group) * RB;
-      const bool ok = rs + (int)threadIdx.x < p.L;
-      ls[threadIdx.x] = ok ? sg.lse * 1.4426950408889634f : INFINITY;
-      ls[RB + threadIdx.x] = ok ? sg.dsum : 0.f;
+      float* ls = (float*)(buf + 2 * LY::T_BYTES);
+      const bool ok = lse_ok;
+      ls[threadIdx.x] = ok ? lse_r * 1.4426950408889634f : INFINITY;
+      ls[RB + threadIdx.x] = ok ? d_r : 0.f;
     }
   };
 
-  f32x16 dkacc[NDB], dvacc[NDB];
+  char* xp = smem + 2 * LY::BUF_BYTES;        // P of the 128 keys, [key][row]
+  char* xd = xp + LY::X_BYTES;                // dS
+  f32x16 dkacc[NDBH], dvacc[NDBH];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) { dkacc[db] = f32x16{}; dvacc[db] = f32x16{}; }
+  for (int db = 0; db < NDBH; ++db) { dkacc[db] = f32x16{}; dvacc[db] = f32x16{}; }
   const int g = lane >> 4, li = lane & 15;
 
-  // S = Q K^T and dP = dO V^T of iteration it: RB rows x this wave's 32 keys
-  // (lane = key) into s[0..QB) (S) and s[QB..2QB) (dP); operand reads PD ahead.
-  f32x16 s[2 * QB];
-  auto sdp = [&](int it) {
-    const char* base = smem + tbuf(it) + (qn * STR + hh * 8) * 2;
-    // MFMA i: S (i even) or dP (i odd), so that consecutive MFMAs never
-    // accumulate into the same registers; kk = i / (2 QB), qb = (i / 2) % QB
+  // ---- phase A(it): S, dP for rows [32 hf, 32 hf + 32) x this lane's key
+  // (lane = key; S and dP alternate so that consecutive MFMAs are
+  // independent, operand reads PD ahead), then P = exp2(scale_log2 S - lse2)
+  // on the rows that see the key and dS = P (dP - D); register r holds local
+  // row 32 hf + 8(r/4) + 4 hh + r%4.  P, dS go to LDS per key in the order
+  // the row contraction consumes them: its B slot s of a lane with
+  // hh = l/32 must hold row 16c + 8(s/4) + 4 hh + s%4 (the row the
+  // transposing read puts in A slot s), so within each 16-row chunk the rows
+  // are stored as 0-3, 8-11, 4-7, 12-15 and a lane reads its 8 values at
+  // position 16c + 8 hh with one 16-byte read.
+  int a_rs = j_first, a_h = 0;  // row block of the next phase_a call (called for it = 0, 1, ...)
+  auto phase_a = [&](int it) {
+    const char* buf = smem + tbuf(it);
+    const int rs = a_rs;
+    if (++a_h == group) { a_h = 0; a_rs += RB; }
+    constexpr int NS = 2 * NKK, PD = 4;
+    const char* base = buf + ((32 * hf + qn) * STR + hh * 8) * 2;
     auto opnd = [&](int i) -> bf16x8 {
-      const int kk = i / (2 * QB), qb = (i / 2) % QB;
-      const int off = ((i & 1) ? LY::T_BYTES : 0) + (qb * 32 * STR + kk * 16) * 2;  // Q for S, dO for dP
-      return *(const bf16x8*)(base + off);
+      return *(const bf16x8*)(base + ((i & 1) ? LY::T_BYTES : 0) + (i >> 1) * 32);
     };
-    constexpr int PD = 4;
+    f32x16 sacc = f32x16{}, dpacc = f32x16{};
     bf16x8 op[NS];
 #pragma unroll
     for (int i = 0; i < PD; ++i) op[i] = opnd(i);
 #pragma unroll
-    for (int x = 0; x < 2 * QB; ++x) s[x] = f32x16{};
-#pragma unroll
     for (int i = 0; i < NS; ++i) {
       if (i + PD < NS) op[i + PD] = opnd(i + PD);
-      const int kk = i / (2 * QB), qb = (i / 2) % QB;
-      if (i & 1) s[QB + qb] = mfma32x16(op[i], vreg[kk], s[QB + qb]);
-      else s[qb] = mfma32x16(op[i], kreg[kk], s[qb]);
+      if (i & 1) dpacc = mfma32x16(op[i], vreg[i >> 1], dpacc);
+      else sacc = mfma32x16(op[i], kreg[i >> 1], sacc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // lse2 and D of this lane's rows: four runs of 4 consecutive rows
+    const float* ls = (const float*)(buf + 2 * LY::T_BYTES) + 32 * hf + 4 * hh;
+    f32x4 l2[4], dd[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      l2[q4] = *(const f32x4*)(ls + 8 * q4);
+      dd[q4] = *(const f32x4*)(ls + RB + 8 * q4);
+    }
+    // The key is seen by the local rows [lo, lo + width); element r of this
+    // lane is local row lr0 + 8(r/4) + r%4.  Blocks where it sees all of this
+    // lane's rows skip the test (a wave-uniform branch).
+    const int lr0 = 32 * hf + 4 * hh;
+    const int lo = my_key - rs - lr0;
+    const uint32_t width = (uint32_t)max(key_hi - my_key, 0);
+    char* pw = xp + ((kg * 32 + qn) * PSTR + 32 * hf + 8 * hh) * 2;
+    char* dw = xd + ((kg * 32 + qn) * PSTR + 32 * hf + 8 * hh) * 2;
+    auto pds = [&](bool masked) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        bf16x4 pv, dv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          float pr = fast_exp2(__builtin_fmaf(sacc[r], p.scale_log2, -l2[q4][e]));
+          if (masked) pr = (uint32_t)(8 * q4 + e - lo) < width ? pr : 0.f;
+          pv[e] = (bf16)pr;
+          dv[e] = (bf16)(pr * (dpacc[r] - dd[q4][e]));
+        }
+        const int pos = 16 * (q4 >> 1) + 4 * (q4 & 1);  // rows 8 q4 + 4 hh + 0..3 of this wave's 32
+        *(bf16x4*)(pw + pos * 2) = pv;
+        *(bf16x4*)(dw + pos * 2) = dv;
+      }
+    };
+    if (__all(lo <= 0 && (uint32_t)(27 - lo) < width)) pds(false);
+    else pds(true);
+  };
+
+  // ---- phase B(it): dV^T += dO^T P, dK^T += Q^T dS over the 64 rows for
+  // head dims [HD hf, HD hf + HD): A through transposing reads of the
+  // tiles, B = P, dS of this key group (lane l: key l % 32, the 8 rows at
+  // position 16c + 8(l / 32)); operand reads PD MFMAs ahead.
+  auto phase_b = [&](int it) {
+    const char* buf = smem + tbuf(it);
+    const char* abase = buf + ((4 * (g >> 1) + (li >> 2)) * STR + HD * hf + 16 * (g & 1) + 4 * (li & 3)) * 2;
+    const char* pb = xp + ((kg * 32 + qn) * PSTR + 8 * hh) * 2;
+    const char* sb = xd + ((kg * 32 + qn) * PSTR + 8 * hh) * 2;
+    constexpr int NB = (RB / 16) * NDBH * 2, PD = 4;  // MFMA i: chunk c, block db, dV (even) / dK (odd)
+    auto opnd = [&](int i) -> bf16x8 {
+      const int c = i / (2 * NDBH), db = (i >> 1) % NDBH;
+      const int off = ((i & 1) ? 0 : LY::T_BYTES) + (16 * c * STR + 32 * db) * 2;  // dO for dV, Q for dK
+      const bf16x4 lo4 = lds_read_tr16(abase + off);
+      const bf16x4 hi4 = lds_read_tr16(abase + off + 8 * STR * 2);
+      return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    };
+    auto bop = [&](int i) -> bf16x8 {
+      const int c = i / (2 * NDBH);
+      return *(const bf16x8*)(((i & 1) ? sb : pb) + 16 * c * 2);
+    };
+    bf16x8 op[NB], bo[NB];
+#pragma unroll
+    for (int i = 0; i < PD; ++i) { op[i] = opnd(i); bo[i] = bop(i); }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      if (i + PD < NB) { op[i + PD] = opnd(i + PD); bo[i + PD] = bop(i + PD); }
+      const int db = (i >> 1) % NDBH;
+      if (i & 1) dkacc[db] = mfma32x16(op[i], bo[i], dkacc[db]);
+      else dvacc[db] = mfma32x16(op[i], bo[i], dvacc[db]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // P, dS of iteration it (element e of this lane's NE) from s and the rows'
-  // lse2, D, as the B operands of the row contraction: chunk c holds rows
-  // 16c .. 16c + 15, slot sl is register (c & 1) * 8 + sl of block c >> 1.
-  // This lane's key is seen by the local rows [lo, hi) of the block (its
-  // position, the end of the sequence and, for plain keys, the window), so
-  // the mask is two compares per element and no branch.
-  struct PdS {
-    bf16x8 p[RB / 16], d[RB / 16];
-  };
-  const int key_hi = !key_ok ? -1 : anchors ? p.L : min(p.L, my_key + p.n);  // rows [my_key, key_hi)
-  auto pds = [&](PdS& o, const float* ls, int lo, int hi, int e, bool masked) {
-    const int qb = e / 16, r = e % 16;
-    const int rl0 = qb * 32 + 8 * (r >> 2) + (r & 3);  // local row is rl0 + 4 * hh
-    const int rl = rl0 + 4 * hh;
-    float pr = fast_exp2(__builtin_fmaf(s[qb][r], p.scale_log2, -ls[rl]));
-    if (masked) pr = (rl0 >= lo && rl0 < hi) ? pr : 0.f;
-    const float dsv = pr * (s[QB + qb][r] - ls[RB + rl]);
-    const int c = qb * 2 + (r >> 3), sl = r & 7;
-    o.p[c][sl] = (bf16)pr;
-    o.d[c][sl] = (bf16)dsv;
-    if (sl & 1) {
-      // Pin the finished pair here: without a use at this point the compiler
-      // sinks the whole P/dS computation to the end of the step (its first
-      // real use is the next step's MFMAs), out of reach of the interleave.
-      const uint32_t pw = __builtin_bit_cast(u32x4, o.p[c])[sl >> 1];
-      const uint32_t dw = __builtin_bit_cast(u32x4, o.d[c])[sl >> 1];
-      asm volatile("" ::"v"(pw), "v"(dw));
+  fetch(0);
+  store(0);
+  fetch(1);
+  __syncthreads();
+
+  if (half == 1) __syncthreads();  // the second half runs one phase behind
+  for (int it = 0; it < n_it; ++it) {
+    phase_a(it);
+    if (half == 1) {  // tile it + 1 over tile it - 1, tile it + 2 in flight
+      store(it + 1);
+      fetch(it + 2);
     }
-  };
-  auto pds_range = [&](int it, int& lo, int& hi) {  // in units of rl0 (hh folded in)
-    const int rs = j_first + (it / group) * RB;
-    lo = my_key - rs - 4 * hh;
-    hi = key_hi - rs - 4 * hh;
-  };
-
-  // dV^T += dO^T P and dK^T += Q^T dS for iteration it - 1 (transposing
-  // reads of its tile, P/dS in prev), interleaved with the P/dS of iteration
-  // it into cur (EPM elements per MFMA).  Past the last iteration the P/dS
-  // are formed from stale registers and never used.
-  auto dvdk_pds = [&](int it, const PdS& prev, PdS& cur) {
-    const char* pbuf = smem + tbuf(it + 2);  // tile it - 1
-    const float* ls = (const float*)(smem + tbuf(it) + 2 * LY::T_BYTES);
-    int lo, hi;
-    pds_range(it, lo, hi);
-    // lane li of group g reads row 16c + 4(g/2) + li/4 (and that + 8) at
-    // dims db*32 + 16(g%2) + 4(li%4): a per-lane base plus constant offsets
-    const char* base = pbuf + ((4 * (g >> 1) + (li >> 2)) * STR + 16 * (g & 1) + 4 * (li & 3)) * 2;
-    auto opnd = [&](int i) -> bf16x8 {
-      const int c = i / (2 * NDB), db = (i / 2) % NDB;
-      const int off = ((i & 1) ? 0 : LY::T_BYTES) + (16 * c * STR + db * 32) * 2;  // Q for dK, dO for dV
-      const bf16x4 lo4 = lds_read_tr16(base + off);
-      const bf16x4 hi4 = lds_read_tr16(base + off + 8 * STR * 2);
-      return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-    };
-    auto run = [&](bool masked) {
-      constexpr int PD = 4;
-      bf16x8 op[NC];
-#pragma unroll
-      for (int i = 0; i < PD; ++i) op[i] = opnd(i);
-#pragma unroll
-      for (int i = 0; i < NC; ++i) {
-        if (i + PD < NC) op[i + PD] = opnd(i + PD);
-        const int c = i / (2 * NDB), db = (i / 2) % NDB;
-        if (i & 1) dkacc[db] = mfma32x16(op[i], prev.d[c], dkacc[db]);
-        else dvacc[db] = mfma32x16(op[i], prev.p[c], dvacc[db]);
-#pragma unroll
-        for (int e = 0; e < EPM; ++e) pds(cur, ls, lo, hi, i * EPM + e, masked);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    run(true);
-  };
-
-  // ---- prologue: tile 0 in LDS, tile 1 in registers; step 0 = S, dP and
-  // P, dS of iteration 0
-  PdS pa, pb2;
-  Stage sg;
-  fetch(sg, 0);
-  store(sg, 0);
-  fetch(sg, 1);
-  __syncthreads();
-  sdp(0);
-  {
-    const float* ls = (const float*)(smem + 2 * LY::T_BYTES);
-    int lo, hi;
-    pds_range(0, lo, hi);
-#pragma unroll
-    for (int e = 0; e < NE; ++e) pds(pa, ls, lo, hi, e, true);
-  }
-  store(sg, 1);
-  fetch(sg, 2);
-  __syncthreads();
-
-  // ---- step it (1 <= it < n_it): S, dP of it; P, dS of it beside dV, dK of
-  // it - 1; tile it + 1 into LDS and tile it + 2 into the staging registers.
-  // Unrolled by two so the P/dS register sets alternate without copies.
-  auto step = [&](int it, const PdS& prev, PdS& cur) {
-    sdp(it);
-    dvdk_pds(it, prev, cur);
-    store(sg, it + 1);
-    fetch(sg, it + 2);
     __syncthreads();
-  };
-  int it = 1;
-  for (; it + 1 < n_it; it += 2) {
-    step(it, pa, pb2);
-    step(it + 1, pb2, pa);
+    phase_b(it);
+    if (half == 0) {
+      store(it + 1);
+      fetch(it + 2);
+    }
+    __syncthreads();
   }
-  // (the final dV, dK step also forms P, dS of a block past the end; unused)
-  if (it < n_it) {
-    step(it, pa, pb2);
-    dvdk_pds(it + 1, pb2, pa);
-  } else {
-    dvdk_pds(it, pa, pb2);
-  }
+  if (half == 0) __syncthreads();
 
   if (key_ok) {
-    bf16* dkrow = p.dk + b * p.sk[0] + kvh * p.sk[1] + (int64_t)my_key * p.sk[2];
-    bf16* dvrow = p.dv + b * p.sv[0] + kvh * p.sv[1] + (int64_t)my_key * p.sv[2];
+    bf16* dkrow = p.dk + b * p.sk[0] + kvh * p.sk[1] + (int64_t)my_key * p.sk[2] + HD * hf;
+    bf16* dvrow = p.dv + b * p.sv[0] + kvh * p.sv[1] + (int64_t)my_key * p.sv[2] + HD * hf;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int db = 0; db < NDBH; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int dim = db * 32 + 8 * i + 4 * hh;
@@ -522,11 +519,11 @@ int launch_dq(const BwdParams& p, hipStream_t st) {
 
 template <int D>
 int launch_dkdv(const BwdParams& p, hipStream_t st) {
-  const int smem = 3 * DkvLayout<D>::BUF_BYTES;
+  const int smem = DkvLayout<D>::SMEM;
   auto kern = dkdv_kernel<D>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return sepattn_hip_check(e, "dkdv smem attribute");
-  hipLaunchKernelGGL(kern, dim3(p.B * p.Hkv * 2 * p.n_key_tiles), dim3(256), smem, st, p);
+  hipLaunchKernelGGL(kern, dim3(p.B * p.Hkv * 2 * p.n_key_tiles), dim3(512), smem, st, p);
   return sepattn_hip_check(hipGetLastError(), "dkdv launch");
 }
 
