@@ -260,12 +260,12 @@ def main():
     }
     dec_launch_us = t_dec * 1e3 / (dec.wl.T * args.layers)
     per_launch_bytes = dec.bytes / (dec.wl.T * args.layers)
-    r_dec = {"kernel": "attend_part (fused SepCache step, one layer, d=128, 4 q heads per KV head)",
+    r_dec = {"kernel": "decode_tiles (SepCache step: append, evict, attend; one layer, d=128, 4 q heads per KV head)",
              "bound": "hbm", "achieved": round(per_launch_bytes / (dec_launch_us * 1e-6) / 1e9, 1),
              "peak": PEAK_HBM_GBS, "unit": "GB/s",
              "frac": round(per_launch_bytes / (dec_launch_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
              "per_launch_bytes": round(per_launch_bytes), "avg_launch_us": round(dec_launch_us, 3)}
-    r_fwd = {"kernel": "fwd_kernel (bf16, d=128)", "bound": "mfma", "achieved": round(fwd_tf, 2),
+    r_fwd = {"kernel": "fwd_pp_kernel (bf16, d=128)", "bound": "mfma", "achieved": round(fwd_tf, 2),
              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
              "traffic": None, "per_launch_flops": pre.fwd_flops, "avg_launch_ms": round(t_fwd, 4)}
     r_bwd = {"kernel": "dq_kernel + dkdv_kernel (bf16, d=128)", "bound": "mfma", "achieved": round(bwd_tf, 2),

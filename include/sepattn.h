@@ -21,8 +21,7 @@
  *     PyTorch tensors).  The library never allocates or frees device memory.
  *     Pointers documented as "host" are read before the call returns.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *     enqueues work on it and returns; none waits for the device, except
- *     sepcache_rope_table, which copies a host table and waits for the copy.
+ *     enqueues work on it and returns; none waits for the device.
  *   - The return value is a status code (SEPATTN_OK = 0 or a negative error).
  *     Arguments are validated before any launch; on error nothing is
  *     enqueued and sepattn_last_error() gives a description (per thread).
@@ -187,7 +186,8 @@ typedef struct {
 
 /* Physical slots per stream and KV head: a + s + n + 1. */
 SEPATTN_API int sepcache_slots(int a, int s, int n);
-/* Empty every stream (slot_pos = -1, counters 0) of every KV head. */
+/* Empty every stream (slot_pos = -1, counters 0, K and V zero) of every KV
+ * head. */
 SEPATTN_API int sepcache_reset(const sepcache* c, void* stream);
 /* Append token t of every stream: k_new, v_new bf16 [B, Hkv, d] contiguous,
  * is_sep device uint8 [B].  Token t < a becomes a sink, later tokens enter the
@@ -207,15 +207,22 @@ SEPATTN_API int sepcache_push(const sepcache* c, const void* k_new, const void* 
  * shift == 0: original token positions.
  *   q bf16 [B, Hq, d] (before RoPE), o bf16 [B, Hq, d], contiguous;
  *   Hq / Hkv in {1, 2, 4, 8}.
- * RoPE angles are computed on the device with the position times the
- * frequency reduced modulo one turn in double precision, so any position is
- * exact to fp32 rounding of the reduced angle.  The cache is only read.
- * Caches of up to 384 (d = 128) or 768 (d = 64) slots run as one kernel with
- * one workgroup per (stream, KV head) and need no workspace; larger caches
- * split the slots over several workgroups and merge their partial results in
- * a second kernel.  workspace: sepcache_decode_workspace_size() bytes of
- * device memory (0 for the one-kernel case, where NULL is accepted; no
- * initialisation needed); calls that share a workspace must not overlap.
+ * RoPE angles are computed on the device: position times frequency is
+ * reduced modulo one turn in double precision for original positions and in
+ * fp32 for ranks.  The cache is only read.
+ * Caches with at most 1024 rows (a + s + n + 1, plus the appended token's row
+ * for sepcache_step) run as one kernel: the rows are shared by
+ * ceil(rows / 256) workgroups per (stream, KV head), and with more than one
+ * the last to finish merges the others' partial results from the workspace.
+ * There the rotated keys and query enter the score product as bf16 and the
+ * probabilities enter P V as bf16, both with fp32 sums.  Larger caches split
+ * the rows over workgroups of at most 64 (d = 128) or 128 (d = 64) rows and
+ * merge in a second kernel.  K and V of slots that hold no entry must be
+ * finite (sepcache_reset zeroes them; later they only receive tokens' K and
+ * V).  workspace: sepcache_decode_workspace_size() bytes of device memory (0
+ * when one workgroup per (stream, KV head) suffices, where NULL is accepted),
+ * zero-filled before its first use; the calls leave it ready for the next.
+ * Calls that share a workspace must not overlap.
  * Decode before any append writes zeros. */
 SEPATTN_API size_t sepcache_decode_workspace_size(const sepcache* c, int Hq);
 SEPATTN_API int sepcache_decode(const sepcache* c, int Hq, const void* q, float scale, int shift,

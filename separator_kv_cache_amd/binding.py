@@ -180,7 +180,7 @@ class SepCache:
     def workspace(self, Hq: int) -> torch.Tensor:
         need = _lib.load().sepcache_decode_workspace_size(ctypes.byref(self.c), Hq)
         if self._ws is None or self._ws.numel() < need:
-            self._ws = torch.empty(max(need, 16), dtype=torch.uint8, device=self.k.device)
+            self._ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=self.k.device)
         return self._ws
 
     def decode(self, q, scale: float | None = None, shift: bool = True, out=None):

@@ -138,11 +138,33 @@ __device__ __forceinline__ void commit(const Transition& tr, int32_t* st, int32_
   store_counters(st, c);
 }
 
+constexpr int MAX_HALF = 64;  // d/2 for d = 128
+
+// RoPE revolutions per position of each frequency: theta^(-2i/d) / (2 pi).
+struct RopeFreqs {
+  double rev[MAX_HALF];
+};
+
+RopeFreqs rope_freqs(const sepcache* c) {
+  RopeFreqs f;
+  const double two_pi = 6.283185307179586476925286766559;
+  for (int i = 0; i < MAX_HALF; ++i) f.rev[i] = i < c->d / 2 ? pow((double)c->theta, -2.0 * i / c->d) / two_pi : 0.0;
+  return f;
+}
+
 __global__ void reset_kernel(CacheParams p) {
   const size_t bh = blockIdx.x;
   for (int i = threadIdx.x; i < p.slots; i += blockDim.x) {
     p.slot_pos[bh * p.slots + i] = -1;
     p.slot_sep[bh * p.slots + i] = 0;
+  }
+  // K and V of every slot to zero: decode multiplies the rows that hold no
+  // entry by a zero probability, which must not meet a non-finite value
+  const size_t chunks = (size_t)p.slots * p.d / 8;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (size_t i = threadIdx.x; i < chunks; i += blockDim.x) {
+    st16(p.k + bh * p.slots * p.d + i * 8, z);
+    st16(p.v + bh * p.slots * p.d + i * 8, z);
   }
   if (threadIdx.x < 8) p.state[bh * 8 + threadIdx.x] = 0;
 }
@@ -206,26 +228,11 @@ __global__ void export_kernel(CacheParams p, int32_t* pos, int32_t* len) {
 
 // ---------------------------------------------------------------- attention
 //
-// Two kernels per decode (or step):
-//  * attend_part: workgroup = (stream, KV head, split) over at most 64 (d=128)
-//    or 128 (d=64) rows.  Rows are the physical slots plus, for a step, one
-//    virtual row holding the new token (read from the inputs).  A group of
-//    D/8 lanes takes one row; lane li holds dimensions [4li, 4li+4) and their
-//    RoPE partners [D/2 + 4li, D/2 + 4li + 4).  Every load is issued before
-//    the counters are used (none of the addresses depends on them), and RoPE
-//    angles are computed in the kernel, so a split costs one memory round
-//    trip.  Each split writes its (o, sum, max) partial; for a step, the
-//    lanes holding the new token and the evicted separator also write those
-//    rows to their new slots (slots no other split needs in this step).
-//  * attend_merge: workgroup = (stream, KV head): merges the partials in split
-//    order and writes o; for a step it then commits slot metadata and
-//    counters.
-
-constexpr int SPLIT_THREADS = 256;   // split path: rows per split = 256/(d/8) * 4
-constexpr int SPLIT_MAXR = 4;
-constexpr int FUSED_THREADS = 512;   // fused path: up to 512/(d/8) * 12 rows
-constexpr int FUSED_MAXR = 12;
-constexpr int MAX_HALF = 64;    // d/2 for d = 128
+// Caches of at most DT_MAX_ROWS rows (the physical slots, plus the appended
+// token's row in a step) run as one kernel, decode_tiles, with one workgroup
+// per (stream, KV head).  Larger caches split their rows over several
+// attend_part workgroups that each write an (o, sum, max) partial, and
+// attend_merge combines them.
 
 struct AttendParams {
   CacheParams c;
@@ -234,8 +241,8 @@ struct AttendParams {
   const bf16* k_new;
   const bf16* v_new;
   const uint8_t* is_sep;
-  float* part;  // [B, Hkv, split, G, D + 2]: o, sum, max
-  int Hq, shift, split;
+  float* part;  // workspace: partial results (and, tiled path, tickets)
+  int Hq, shift, split, tiled;
   float scale_log2;
   double rev[MAX_HALF];  // theta^(-2i/d) / (2 pi): RoPE revolutions per position
 };
@@ -258,18 +265,51 @@ __device__ __forceinline__ void rope_cs(int pos, double rev, float rev32, float&
   s = __builtin_amdgcn_sinf(f);
 }
 
-// FUSED: one workgroup holds every row of its (stream, KV head) (split ==
-// 1): it normalises and writes o itself and, for a step, commits the slot
-// metadata and counters after its last read of them.
-template <int D, int G, bool UPDATE, bool SHIFT, int NT, int MAXR, bool FUSED>
-__global__ __launch_bounds__(NT) void attend_part(AttendParams p) {
-  constexpr int AT_THREADS = NT;
-  constexpr int AT_MAXR = MAXR;
+// Rank after the step of physical row `row` (row == slots: the appended
+// token), or -1 if the row holds no entry then.
+template <bool UPDATE>
+__device__ __forceinline__ int row_rank(int row, const Counters& c0, const Transition& tr, int a, int s, int n,
+                                        int slots) {
+  const Counters& c1 = tr.after;
+  if (row >= slots) return (UPDATE && row == slots && tr.app_slot >= 0) ? c1.nsink + c1.sepc + c1.winc - 1 : -1;
+  if (row < a) return row < c0.nsink ? row : -1;
+  if (row < a + s) {
+    int off = row - a - c0.seph;
+    if (off < 0) off += s;
+    if (off >= c0.sepc) return -1;
+    if (tr.sep_drop) return off == 0 ? -1 : c1.nsink + off - 1;
+    return c1.nsink + off;
+  }
+  int off = row - a - s - c0.winh;
+  if (off < 0) off += n + 1;
+  if (off >= c0.winc) return -1;
+  if (tr.evicted) {
+    if (off == 0) return tr.ev_dst >= 0 ? c1.nsink + c1.sepc - 1 : -1;
+    return c1.nsink + c1.sepc + off - 1;
+  }
+  return c1.nsink + c1.sepc + off;
+}
+
+// ---- split path: workgroup = (stream, KV head, split) over at most 64 (d=128)
+// or 128 (d=64) rows.  A group of D/8 lanes takes one row; lane li holds
+// dimensions [4li, 4li+4) and their RoPE partners [D/2 + 4li, D/2 + 4li + 4).
+// Every load is issued before the counters are used, and RoPE angles are
+// computed in the kernel, so a split costs one memory round trip.  For a
+// step, the lanes holding the new token and the evicted separator also write
+// those rows to their new slots (slots no other split reads this step);
+// attend_merge commits the slot metadata and counters.
+
+constexpr int SPLIT_THREADS = 256;  // rows per split = 256/(d/8) * 4
+constexpr int SPLIT_MAXR = 4;
+
+template <int D, int G, bool UPDATE, bool SHIFT>
+__global__ __launch_bounds__(SPLIT_THREADS) void attend_part(AttendParams p) {
   constexpr int LPR = D / 8;
-  constexpr int GROUPS = AT_THREADS / LPR;
+  constexpr int GROUPS = SPLIT_THREADS / LPR;
   constexpr int HALF = D / 2;
-  constexpr int NW = AT_THREADS / 64;
-  __shared__ float sc[G][GROUPS * AT_MAXR];
+  constexpr int NW = SPLIT_THREADS / 64;
+  constexpr int MAXR = SPLIT_MAXR;
+  __shared__ float sc[G][GROUPS * MAXR];
   __shared__ float red[NW][G];
   __shared__ float mstat[G];
   __shared__ float acc[NW][G][D];
@@ -287,15 +327,15 @@ __global__ __launch_bounds__(NT) void attend_part(AttendParams p) {
   const int row0 = split * per, row1 = min(rows, row0 + per);
 
   // ---- every load first: slot positions (no shift), K/V rows, queries
-  int spos_r[AT_MAXR];
+  int spos_r[MAXR];
   if constexpr (!SHIFT) {
 #pragma unroll
-    for (int r = 0; r < AT_MAXR; ++r)
+    for (int r = 0; r < MAXR; ++r)
       spos_r[r] = c.slot_pos[(size_t)bh * c.slots + min(row0 + grp + r * GROUPS, c.slots - 1)];
   }
-  bf16x4 klo[AT_MAXR], khi[AT_MAXR], vlo[AT_MAXR], vhi[AT_MAXR];
+  bf16x4 klo[MAXR], khi[MAXR], vlo[MAXR], vhi[MAXR];
 #pragma unroll
-  for (int r = 0; r < AT_MAXR; ++r) {
+  for (int r = 0; r < MAXR; ++r) {
     const int row = min(row0 + grp + r * GROUPS, rows - 1);
     const bool cached = row < c.slots;
     const bf16* ks = cached ? kb + (size_t)row * D : p.k_new + (size_t)bh * D;
@@ -326,38 +366,11 @@ __global__ __launch_bounds__(NT) void attend_part(AttendParams p) {
   const Transition tr = transition(c0, c.a, c.s, c.n, UPDATE, new_sep, UPDATE);
   const Counters c1 = tr.after;
   const int total = c1.nsink + c1.sepc + c1.winc;
-  const int W = c.n + 1;
-  // offsets within a ring without integer division: x lies in (-m, m)
-  auto wrap = [](int x, int m) { return x < 0 ? x + m : x; };
-  auto rank_of = [&](int row) -> int {
-    if (row >= c.slots) return (UPDATE && tr.app_slot >= 0) ? total - 1 : -1;  // the new token
-    if (row < c.a) return row < c0.nsink ? row : -1;
-    if (row < c.a + c.s) {
-      const int off = wrap(row - c.a - c0.seph, c.s);
-      if (off >= c0.sepc) return -1;
-      if (tr.sep_drop) return off == 0 ? -1 : c1.nsink + off - 1;
-      return c1.nsink + off;
-    }
-    const int off = wrap(row - c.a - c.s - c0.winh, W);
-    if (off >= c0.winc) return -1;
-    if (tr.evicted) {
-      if (off == 0) return tr.ev_dst >= 0 ? c1.nsink + c1.sepc - 1 : -1;
-      return c1.nsink + c1.sepc + off - 1;
-    }
-    return c1.nsink + c1.sepc + off;
-  };
-  int ev_pos = -1, new_oldsep = 0;
-  if constexpr (FUSED && UPDATE) {
-    if (threadIdx.x == 0) {
-      if (tr.evicted) ev_pos = c.slot_pos[(size_t)bh * c.slots + tr.ev_src];
-      if (tr.refresh_oldsep) new_oldsep = c.slot_sep[(size_t)bh * c.slots + c.a + c.s + c1.winh];
-    }
-  }
-  int kpos[AT_MAXR];
+  int kpos[MAXR];
 #pragma unroll
-  for (int r = 0; r < AT_MAXR; ++r) {
+  for (int r = 0; r < MAXR; ++r) {
     const int row = row0 + grp + r * GROUPS;
-    const int rk = row < row1 ? rank_of(row) : -1;
+    const int rk = row < row1 ? row_rank<UPDATE>(row, c0, tr, c.a, c.s, c.n, c.slots) : -1;
     if constexpr (SHIFT) kpos[r] = rk;
     else kpos[r] = rk < 0 ? -1 : (row < c.slots ? spos_r[r] : c1.t - 1);
   }
@@ -384,7 +397,7 @@ __global__ __launch_bounds__(NT) void attend_part(AttendParams p) {
 #pragma unroll
   for (int h = 0; h < G; ++h) mloc[h] = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < AT_MAXR; ++r) {
+  for (int r = 0; r < MAXR; ++r) {
     const int pos = kpos[r];
     float part[G];
 #pragma unroll
@@ -423,8 +436,8 @@ __global__ __launch_bounds__(NT) void attend_part(AttendParams p) {
   }
   __syncthreads();
   // probabilities, once per (row, head)
-  for (int idx = threadIdx.x; idx < G * GROUPS * AT_MAXR; idx += AT_THREADS) {
-    const int h = idx / (GROUPS * AT_MAXR), rr = idx % (GROUPS * AT_MAXR);
+  for (int idx = threadIdx.x; idx < G * GROUPS * MAXR; idx += SPLIT_THREADS) {
+    const int h = idx / (GROUPS * MAXR), rr = idx % (GROUPS * MAXR);
     sc[h][rr] = fast_exp2(sc[h][rr] - mstat[h]);
   }
   __syncthreads();
@@ -438,7 +451,7 @@ __global__ __launch_bounds__(NT) void attend_part(AttendParams p) {
     for (int e = 0; e < 4; ++e) olo[h][e] = ohi[h][e] = 0.f;
   }
 #pragma unroll
-  for (int r = 0; r < AT_MAXR; ++r) {
+  for (int r = 0; r < MAXR; ++r) {
     if (kpos[r] < 0) continue;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -482,19 +495,8 @@ __global__ __launch_bounds__(NT) void attend_part(AttendParams p) {
 #pragma unroll
     for (int h = 0; h < G; ++h) red[wave][h] = lsum[h];
   __syncthreads();
-  if constexpr (FUSED) {
-    for (int idx = threadIdx.x; idx < G * D; idx += AT_THREADS) {
-      const int h = idx / D, dd = idx % D;
-      float v = 0.f, l = 0.f;
-      for (int w = 0; w < NW; ++w) {
-        v += acc[w][h][dd];
-        l += red[w][h];
-      }
-      p.o[((size_t)b * p.Hq + kvh * G + h) * D + dd] = (bf16)(l > 0.f ? v / l : 0.f);
-    }
-  }
   float* out = p.part + ((size_t)bh * p.split + split) * G * (D + 2);
-  for (int idx = threadIdx.x; !FUSED && idx < G * (D + 2); idx += AT_THREADS) {
+  for (int idx = threadIdx.x; idx < G * (D + 2); idx += SPLIT_THREADS) {
     const int h = idx / (D + 2), dd = idx % (D + 2);
     float v;
     if (dd < D) {
@@ -512,7 +514,7 @@ __global__ __launch_bounds__(NT) void attend_part(AttendParams p) {
   // ---- a step moves the new token and the evicted separator from registers
   if constexpr (UPDATE) {
 #pragma unroll
-    for (int r = 0; r < AT_MAXR; ++r) {
+    for (int r = 0; r < MAXR; ++r) {
       const int row = row0 + grp + r * GROUPS;
       int dst = -1;
       if (row < row1) {
@@ -527,13 +529,6 @@ __global__ __launch_bounds__(NT) void attend_part(AttendParams p) {
         *(bf16x4*)(vd + li * 4) = vlo[r];
         *(bf16x4*)(vd + HALF + li * 4) = vhi[r];
       }
-    }
-    if constexpr (FUSED) {
-      // every read of the old metadata (ranks, positions) happened before the
-      // barriers above; thread 0 holds the two values the commit needs
-      if (threadIdx.x == 0)
-        commit(tr, c.state + (size_t)bh * 8, c.slot_pos + (size_t)bh * c.slots, c.slot_sep + (size_t)bh * c.slots,
-               new_sep, ev_pos, new_oldsep);
     }
   }
 }
@@ -607,37 +602,583 @@ __global__ __launch_bounds__(MERGE_THREADS) void attend_merge(AttendParams p) {
   }
 }
 
-int attend_rows(const sepcache* c, bool update) { return c->a + c->s + c->n + 1 + (update ? 1 : 0); }
-bool attend_fused(const sepcache* c, bool update) {
-  return attend_rows(c, update) <= FUSED_THREADS / (c->d / 8) * FUSED_MAXR;
+// ---- tiled path
+//
+// Workgroups of 8 waves; the rows of one (stream, KV head) are cut into
+// tiles of 16, held by one workgroup of at most DT_TPW tiles or shared by
+// several (larger caches); every wave takes up to three tiles, eight apart.
+// Per tile:
+//  * scores S = K Q^T on 16x16x32 bf16 MFMAs, keys along the rows: lane
+//    (g, col) (g = lane / 16) loads row 16t + col, dimensions 32m + 8g .. +7
+//    for m < D/32, so each RoPE pair (i, i + D/2) lies in one lane; query
+//    heads along the columns.  S lands as lane (g, h): rows 4g .. 4g+3 of
+//    head h, which is also the operand layout P needs below.
+//  * O += P V on 16x16x16 bf16 MFMAs: lane (g, c) loads rows 16t + 4g .. +3,
+//    dimensions 8c .. 8c+7 and transposes that 4x8 block in registers, so
+//    MFMA e takes dimension 8c + e of each column c.
+// K/V addresses are physical rows, so no load waits for the counters.  A
+// wave requests its first tile once the counters and query have arrived
+// (loads queue in order, so those small ones would otherwise wait behind
+// the rows) and each later one just before scoring the previous: a compute
+// unit keeps only so many loads in flight, and a wave blocked on issuing one
+// could not compute meanwhile.  A wave keeps
+// the scores of its tiles and takes one maximum over them; the waves'
+// (o, sum, max) merge through LDS.  With several workgroups per (stream, KV
+// head), each writes that triple to the workspace and the last to arrive
+// (an atomic ticket per (stream, KV head), reset by that workgroup) merges
+// them, writes o and, for a step, commits the slot metadata.
+//
+// RoPE with positions shifted to ranks.  A row's rank is its physical index
+// plus an offset that is constant on a few intervals of rows: the sinks, the
+// two sides of each ring's wrap point, the evicted row that moves to the
+// separator block, and the appended token.  Rotations about the same planes
+// compose, so for row 16t + col of interval k, with rank 16t + col + delta_k,
+//     R(rank) k . R(p_q) q  =  R(col) k . R(p_q - delta_k - 16t) q.
+// Keys turn by their column's angle (a 16-row table in LDS, so a lane's angles
+// are the same for all its tiles) and each (interval, tile) pair gets its own
+// copy of the query turned by the rest, built once per workgroup in LDS.  A
+// tile that meets several intervals runs its score MFMAs once per interval
+// and keeps each row's own result.  With original positions, keys turn by
+// their own angle and the query is one copy.
+//
+// Rows that hold no entry get probability zero; a non-finite value in such a
+// slot would still reach the output through 0 * V in the MFMA, so
+// sepcache_reset zeroes every slot and slots only receive tokens' K and V.
+
+constexpr int DT_WAVES = 8;
+constexpr int DT_THREADS = 64 * DT_WAVES;
+constexpr int DT_ROWS = 16;   // rows per tile
+constexpr int DT_MAXT = 3;    // tiles per wave
+constexpr int DT_TPW = DT_WAVES * DT_MAXT;  // tiles per workgroup
+constexpr int DT_MAX_SPLIT = 4;
+constexpr int DT_MAX_ROWS = DT_MAX_SPLIT * DT_TPW * DT_ROWS;
+constexpr int DT_NCLS = 7;    // intervals of constant rank offset
+constexpr int DT_MAX_VAR = DT_TPW + DT_NCLS - 1;  // (interval, tile) pairs of one workgroup
+constexpr size_t DT_TICKET_BYTES = 256;            // per 64 (stream, KV head) pairs
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// Row intervals [lo, hi) of constant rank - row = delta; a row of interval k
+// holds an entry iff its rank lies in [vlo, vhi).  The (interval, tile) pairs
+// of tiles [t_lo, t_hi) are numbered interval by interval: interval k meets
+// tiles t0 .. and its pairs start at first.
+struct RowClasses {
+  int lo[DT_NCLS], hi[DT_NCLS], delta[DT_NCLS], vlo[DT_NCLS], vhi[DT_NCLS];
+  int first[DT_NCLS], t0[DT_NCLS], n_var;
+};
+
+template <bool UPDATE>
+__device__ __forceinline__ RowClasses row_classes(const Counters& c0, const Transition& tr, int a, int s, int n,
+                                                  int slots, int t_lo, int t_hi) {
+  const Counters& c1 = tr.after;
+  const int drop = tr.sep_drop ? 1 : 0, ev = tr.evicted ? 1 : 0;
+  const int sep0 = a + c0.seph, win0 = a + s + c0.winh;
+  const int sep_rank = c1.nsink, win_rank = c1.nsink + c1.sepc;
+  const int dsep = sep_rank - sep0 - drop, dwin = win_rank - ev - win0;
+  const bool moved = tr.evicted && tr.ev_dst >= 0;
+  const bool app = UPDATE && tr.app_slot >= 0;
+  const int total = c1.nsink + c1.sepc + c1.winc;
+  RowClasses rc;
+  // sinks; separator ring past / before its head; window ring past / before
+  // its head; the evicted row moving to the separator block; the appended token
+  const int lo[DT_NCLS] = {0, a, sep0, a + s, win0 + ev, win0, slots};
+  const int hi[DT_NCLS] = {a, sep0, a + s, win0, slots, win0 + (moved ? 1 : 0), slots + (app ? 1 : 0)};
+  const int dl[DT_NCLS] = {0, dsep + s, dsep, dwin + n + 1, dwin, win_rank - 1 - win0, total - 1 - slots};
+  const int vl[DT_NCLS] = {0, sep_rank, sep_rank, win_rank, win_rank, win_rank - 1, total - 1};
+  const int vh[DT_NCLS] = {c0.nsink, sep_rank + c0.sepc - drop, sep_rank + c0.sepc - drop,
+                           win_rank + c0.winc - ev, win_rank + c0.winc - ev, win_rank, total};
+  int nv = 0;
+#pragma unroll
+  for (int k = 0; k < DT_NCLS; ++k) {
+    rc.lo[k] = lo[k];
+    rc.hi[k] = hi[k];
+    rc.delta[k] = dl[k];
+    rc.vlo[k] = vl[k];
+    rc.vhi[k] = vh[k];
+    rc.first[k] = nv;
+    const int a0 = max(lo[k] / DT_ROWS, t_lo), a1 = min((hi[k] - 1) / DT_ROWS, t_hi - 1);
+    rc.t0[k] = a0;
+    if (hi[k] > lo[k] && a1 >= a0) nv += a1 - a0 + 1;
+  }
+  rc.n_var = nv;
+  return rc;
 }
+
+// Bits of the rows of tile [row0, row0 + 16) that belong to interval k and
+// hold an entry (wave-uniform).
+__device__ __forceinline__ uint32_t class_rows(const RowClasses& rc, int k, int row0) {
+  const int lo = max(max(rc.lo[k], rc.vlo[k] - rc.delta[k]), row0) - row0;
+  const int hi = min(min(rc.hi[k], rc.vhi[k] - rc.delta[k]), row0 + DT_ROWS) - row0;
+  return hi > lo ? ((1u << hi) - 1u) & ~((1u << lo) - 1u) : 0u;
+}
+
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+__device__ __forceinline__ uint32_t pack_bf(float x, float y) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(bf16)x, (bf16)y};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// max(x[l], x[l ^ 16]): v_permlane16_swap exchanges the odd 16-lane rows of
+// its first register with the even rows of its second.
+__device__ __forceinline__ float max_xor16(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
+// Workspace of the tiled path: tickets, then [B * Hkv][split][G][D + 2]
+// partials (o, sum, max).
+__host__ __device__ inline size_t dt_ticket_bytes(int bh) {
+  return ((size_t)bh * 4 + DT_TICKET_BYTES - 1) / DT_TICKET_BYTES * DT_TICKET_BYTES;
+}
+
+template <int D, int G, bool UPDATE, bool SHIFT>
+__global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
+  constexpr int NM = D / 32;  // score MFMAs per tile (k = 32 dimensions each)
+  constexpr int NP = NM / 2;  // chunks m < NP pair with m + NP
+  constexpr int NCH = D / 8;  // 16-byte chunks per row
+  constexpr int HALF = D / 2;
+  constexpr int NQ = SHIFT ? DT_MAX_VAR : 1;  // query copies
+  constexpr int QSTR = D + 8;                 // LDS row of one (copy, head); the pad spreads banks
+  constexpr int TSTR = HALF + 2;              // LDS row of the column angles, likewise
+  __shared__ __attribute__((aligned(16))) bf16 qvar[NQ * G * QSTR];
+  __shared__ __attribute__((aligned(16))) float2 tcol[SHIFT ? DT_ROWS * TSTR : 1];
+  __shared__ float o_w[DT_WAVES][G][D];
+  __shared__ float m_w[DT_WAVES][G], l_w[DT_WAVES][G];
+  __shared__ int last_s;
+
+  const CacheParams& c = p.c;
+  const int BH = c.B * c.Hkv;
+  const int bh = blockIdx.x % BH, split = blockIdx.x / BH;  // splits of one pair are BH apart
+  const int b = bh / c.Hkv, kvh = bh % c.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile branches stay scalar
+  const int g = lane >> 4, col = lane & 15;
+  const int slots = c.slots;
+  const int rows = slots + (UPDATE ? 1 : 0);
+  const int n_tiles = (rows + DT_ROWS - 1) / DT_ROWS;
+  const int tps = (n_tiles + p.split - 1) / p.split;
+  const int t_lo = split * tps, t_hi = min(t_lo + tps, n_tiles);  // this workgroup's tiles
+  const uint32_t row_bytes = D * 2;
+  bf16* kb = c.k + (size_t)bh * slots * D;
+  bf16* vb = c.v + (size_t)bh * slots * D;
+
+  // ---- loads independent of the counters.  Everything the prologue needs
+  // per lane is requested before the K/V rows, so that waiting for it never
+  // waits for them.
+  const int32_t* st = c.state + (size_t)bh * 8;
+  Counters c0;
+  c0.t = __builtin_amdgcn_readfirstlane(st[ST_T]);
+  c0.nsink = __builtin_amdgcn_readfirstlane(st[ST_NSINK]);
+  c0.seph = __builtin_amdgcn_readfirstlane(st[ST_SEPH]);
+  c0.sepc = __builtin_amdgcn_readfirstlane(st[ST_SEPC]);
+  c0.winh = __builtin_amdgcn_readfirstlane(st[ST_WINH]);
+  c0.winc = __builtin_amdgcn_readfirstlane(st[ST_WINC]);
+  c0.flags = __builtin_amdgcn_readfirstlane(st[ST_FLAGS]);
+  c0.oldsep = __builtin_amdgcn_readfirstlane(st[ST_OLDSEP]);
+  const int is_sep_b = UPDATE ? (int)p.is_sep[b] : 0;
+  // the query pair this thread turns in the prologue: dims i and i + D/2 of
+  // copies tid / HALF, tid / HALF + DT_THREADS / HALF, ...
+  const int qi = tid % HALF;
+  const double rev_q = p.rev[qi];
+  float qx1[G], qx2[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const bf16* qr = p.q + ((size_t)b * p.Hq + kvh * G + h) * D;
+    qx1[h] = bf2f(qr[qi]);
+    qx2[h] = bf2f(qr[qi + HALF]);
+  }
+  // original positions: this lane's key frequencies i = 32 m + 8 g + e, m < NP
+  double rev_k[SHIFT ? 1 : NP][8];
+  if constexpr (!SHIFT) {
+#pragma unroll
+    for (int m = 0; m < NP; ++m)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rev_k[m][e] = p.rev[32 * m + 8 * g + e];
+  }
+
+  // wave w takes tiles t_hi-1-w and t_hi-9-w: in a step the last tile, which
+  // holds the appended token's row, is wave 0's first in the last workgroup
+  auto tile_of = [&](int j) {
+    const int t = t_hi - 1 - wave - DT_WAVES * j;
+    return t >= t_lo ? t : -1;
+  };
+  // The appended token's row first (step): rows past the cache read as zeros
+  // below and these loads fill row `slots`.  Every tile load is issued
+  // unconditionally (absent tiles at an offset past the end, which reads
+  // zeros and touches no memory), so that each wait counts exactly the loads
+  // issued after the ones it needs.
+  const bool holds_new = UPDATE && wave == 0 && t_hi == n_tiles;
+  u32x4 kin[NM], vin[4];
+  if (holds_new) {
+    const int krow = (n_tiles - 1) * DT_ROWS + col;
+    const rsrc_t kis = make_rsrc(p.k_new + (size_t)bh * D, row_bytes);
+    const rsrc_t vis = make_rsrc(p.v_new + (size_t)bh * D, row_bytes);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) kin[m] = bld16(kis, krow == slots ? (4 * m + g) * 16 : BUF_OOB);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      vin[u] = bld16(vis, ((n_tiles - 1) * DT_ROWS + 4 * g + u == slots && col < NCH) ? col * 16 : BUF_OOB);
+  }
+  const rsrc_t krs = make_rsrc(kb, (uint32_t)slots * row_bytes);
+  const rsrc_t vrs = make_rsrc(vb, (uint32_t)slots * row_bytes);
+  const rsrc_t prs = make_rsrc(c.slot_pos + (size_t)bh * slots, (uint32_t)slots * 4);
+  u32x4 kr[DT_MAXT][NM], vr[DT_MAXT][4];
+  int spos[DT_MAXT];
+  // An absent tile (t = -1) sets the offsets' top bit arithmetically rather
+  // than by a select, so the compiler neither branches on it nor merges the
+  // identical loads it would produce (either would put a wait here).
+  auto issue = [&](int j) {
+    const int t = tile_of(j);
+    const uint32_t absent = (uint32_t)(t >> 31) & BUF_OOB;
+    const int krow = t * DT_ROWS + col;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) kr[j][m] = bld16(krs, ((uint32_t)krow * row_bytes + (4 * m + g) * 16) | absent);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      vr[j][u] = bld16(vrs, col < NCH ? ((uint32_t)(t * DT_ROWS + 4 * g + u) * row_bytes + col * 16) | absent : BUF_OOB);
+    if constexpr (!SHIFT) spos[j] = bld4(prs, ((uint32_t)krow * 4) | absent);
+  };
+  const bool new_sep = __builtin_amdgcn_readfirstlane(is_sep_b) != 0;
+
+  // ---- counters after the step, row intervals, query copies
+  const Transition tr = transition(c0, c.a, c.s, c.n, UPDATE, new_sep, UPDATE);
+  const Counters c1 = tr.after;
+  const int total = c1.nsink + c1.sepc + c1.winc;
+  int ev_pos = -1, new_oldsep = 0;
+  if constexpr (UPDATE) {
+    if (tid == 0) {
+      if (tr.evicted) ev_pos = c.slot_pos[(size_t)bh * slots + tr.ev_src];
+      if (tr.refresh_oldsep) new_oldsep = c.slot_sep[(size_t)bh * slots + c.a + c.s + c1.winh];
+    }
+  }
+  const RowClasses rc = row_classes<UPDATE>(c0, tr, c.a, c.s, c.n, slots, t_lo, t_hi);
+  issue(0);  // after the small loads above have arrived, so they did not queue behind it
+  {
+    const float rev32 = (float)rev_q;
+    const int n_copies = SHIFT ? min(rc.n_var, DT_MAX_VAR) : 1;
+    for (int v = tid / HALF; v < n_copies; v += DT_THREADS / HALF) {
+      int pos;
+      if constexpr (SHIFT) {
+        // the interval owning copy v: the last non-empty one starting at or before it
+        int at = 0;
+#pragma unroll
+        for (int k = 0; k < DT_NCLS; ++k)
+          if (rc.hi[k] > rc.lo[k] && v >= rc.first[k]) at = rc.delta[k] + (rc.t0[k] + v - rc.first[k]) * DT_ROWS;
+        pos = total - 1 - at;
+      } else {
+        pos = c1.t - 1;
+      }
+      float cs, sn;
+      rope_cs<SHIFT>(pos, rev_q, rev32, cs, sn);
+      cs *= p.scale_log2;
+      sn *= p.scale_log2;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        bf16* dst = qvar + (v * G + h) * QSTR;
+        dst[qi] = (bf16)(qx1[h] * cs - qx2[h] * sn);
+        dst[qi + HALF] = (bf16)(qx2[h] * cs + qx1[h] * sn);
+      }
+    }
+    if constexpr (SHIFT) {
+      for (int idx = tid; idx < DT_ROWS * HALF; idx += DT_THREADS) {  // idx % HALF == qi
+        float cs, sn;
+        rope_cs<true>(idx / HALF, 0.0, rev32, cs, sn);
+        tcol[(idx / HALF) * TSTR + qi] = make_float2(cs, sn);
+      }
+    }
+  }
+  __syncthreads();
+
+  // this lane's key angles (shifted positions): column col, frequencies
+  // i = 32 m + 8 g + e, m < NP
+  float kc[SHIFT ? NP : 1][8], ks[SHIFT ? NP : 1][8];
+  if constexpr (SHIFT) {
+#pragma unroll
+    for (int m = 0; m < NP; ++m)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 v = tcol[col * TSTR + 32 * m + 8 * g + e];
+        kc[m][e] = v.x;
+        ks[m][e] = v.y;
+      }
+  }
+
+  // ---- scores of this wave's tiles
+  f32x4 sco[DT_MAXT];
+#pragma unroll
+  for (int j = 0; j < DT_MAXT; ++j) {
+    if (j + 1 < DT_MAXT) issue(j + 1);
+    const int t = tile_of(j);
+    sco[j] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (t < 0) continue;
+    const int row0 = t * DT_ROWS;
+    const int krow = row0 + col;
+    if (j == 0 && holds_new) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) kr[0][m] |= kin[m];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) vr[0][u] |= vin[u];
+    }
+
+    if constexpr (UPDATE) {  // rows that move: raw K/V to their new slots
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int src = w == 0 ? slots : tr.ev_src;
+        const int dst = w == 0 ? tr.app_slot : tr.ev_dst;
+        if (dst >= 0 && src >= row0 && src < row0 + DT_ROWS) {
+          if (krow == src)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) st16(kb + (size_t)dst * D + (4 * m + g) * 8, kr[j][m]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (row0 + 4 * g + u == src && col < NCH) st16(vb + (size_t)dst * D + col * 8, vr[j][u]);
+        }
+      }
+    }
+
+    // K turned: pairs (m, e) and (m + NP, e)
+    bf16x8 ka[NM];
+    {
+      float y[NM][8];
+#pragma unroll
+      for (int m = 0; m < NP; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t w1 = kr[j][m][e >> 1], w2 = kr[j][m + NP][e >> 1];
+          const float x1 = (e & 1) ? hi_bf(w1) : lo_bf(w1);
+          const float x2 = (e & 1) ? hi_bf(w2) : lo_bf(w2);
+          float cs, sn;
+          if constexpr (SHIFT) {
+            cs = kc[m][e];
+            sn = ks[m][e];
+          } else {
+            const int pos = krow == slots ? c1.t - 1 : spos[j];
+            rope_cs<false>(pos, rev_k[m][e], 0.f, cs, sn);
+          }
+          y[m][e] = x1 * cs - x2 * sn;
+          y[m + NP][e] = x2 * cs + x1 * sn;
+        }
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = pack_bf(y[m][2 * q], y[m][2 * q + 1]);
+        ka[m] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+
+    // one pass per interval the tile meets; each row keeps its own interval's
+    // score, rows that hold no entry keep -inf
+    f32x4 s = sco[j];
+    uint32_t all = 0;
+#pragma unroll
+    for (int k = 0; k < DT_NCLS; ++k) {
+      uint32_t mk = class_rows(rc, k, row0);
+      if constexpr (!SHIFT) {  // one query copy: a single pass over every kept row
+        all |= mk;
+        if (k < DT_NCLS - 1) continue;
+        mk = all;
+      }
+      if (mk == 0) continue;
+      const int v = SHIFT ? min(rc.first[k] + t - rc.t0[k], DT_MAX_VAR - 1) : 0;
+      const bf16* qv = qvar + (v * G + (col & (G - 1))) * QSTR;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        const bf16x8 qb = *(const bf16x8*)(qv + (4 * m + g) * 8);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], qb, acc, 0, 0, 0);
+      }
+      const uint32_t mine = mk >> (4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if ((mine >> r) & 1u) s[r] = acc[r];
+    }
+    sco[j] = s;
+  }
+
+  // ---- this wave's maximum per head (lanes (g, h) hold head h)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < DT_MAXT; ++j) mx = fmaxf(mx, fmaxf(fmaxf(sco[j][0], sco[j][1]), fmaxf(sco[j][2], sco[j][3])));
+  mx = max_xor16(mx);
+  mx = max_xor32(mx);
+  const float mu = mx == -INFINITY ? 0.f : mx;
+
+  // ---- P V
+  f32x4 oacc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) oacc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < DT_MAXT; ++j) {
+    if (tile_of(j) < 0) continue;
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[r] = fast_exp2(sco[j][r] - mu);
+      lsum += pr[r];
+    }
+    const u32x2 pw = {pack_bf(pr[0], pr[1]), pack_bf(pr[2], pr[3])};
+    const i16x4_t pa = __builtin_bit_cast(i16x4_t, pw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const u32x2 vw = {__builtin_amdgcn_perm(vr[j][1][e >> 1], vr[j][0][e >> 1], sel),
+                        __builtin_amdgcn_perm(vr[j][3][e >> 1], vr[j][2][e >> 1], sel)};
+      oacc[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, __builtin_bit_cast(i16x4_t, vw), oacc[e], 0, 0, 0);
+    }
+  }
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+
+  // ---- merge the waves, then the workgroups of this (stream, KV head)
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * g + r;
+    if (h < G && col < NCH)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o_w[wave][h][8 * col + e] = oacc[e][r];
+  }
+  if (g == 0 && col < G) {
+    m_w[wave][col] = mx;
+    l_w[wave][col] = lsum;
+  }
+  __syncthreads();
+  bf16* out = p.o + ((size_t)b * p.Hq + kvh * G) * D;
+  if (p.split == 1) {
+    for (int idx = tid; idx < G * D; idx += DT_THREADS) {
+      const int h = idx / D, d = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < DT_WAVES; ++w) M = fmaxf(M, m_w[w][h]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < DT_WAVES; ++w) {
+          const float f = fast_exp2(m_w[w][h] - M);
+          L += f * l_w[w][h];
+          O += f * o_w[w][h][d];
+        }
+      }
+      out[idx] = (bf16)(L > 0.f ? O / L : 0.f);
+    }
+  } else {
+    int* ticket = (int*)p.part;
+    float* part = (float*)((char*)p.part + dt_ticket_bytes(BH)) + (size_t)bh * p.split * G * (D + 2);
+    for (int idx = tid; idx < G * D; idx += DT_THREADS) {
+      const int h = idx / D, d = idx % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < DT_WAVES; ++w) M = fmaxf(M, m_w[w][h]);
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int w = 0; w < DT_WAVES; ++w) {
+          const float f = fast_exp2(m_w[w][h] - M);
+          L += f * l_w[w][h];
+          O += f * o_w[w][h][d];
+        }
+      }
+      // the partials and the ticket are agent-scope atomics: they are
+      // performed at the device's coherence point, with no cache-wide
+      // write-back or invalidation
+      float* ps = part + ((size_t)split * G + h) * (D + 2);
+      __hip_atomic_store(ps + d, O, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0) {
+        __hip_atomic_store(ps + D, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ps + D + 1, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    // every store of this workgroup has completed (reached the coherence
+    // point) before the ticket is taken; the fence keeps the compiler from
+    // moving them past the wait
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+      const int seen = __hip_atomic_fetch_add(ticket + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = seen == p.split - 1;
+      if (last) __hip_atomic_store(ticket + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_s = last;
+    }
+    __syncthreads();
+    if (!last_s) return;
+    auto rd = [](const float* x) { return __hip_atomic_load(x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    for (int idx = tid; idx < G * D; idx += DT_THREADS) {
+      const int h = idx / D, d = idx % D;
+      float ms[DT_MAX_SPLIT], ls[DT_MAX_SPLIT], os[DT_MAX_SPLIT];
+      float M = -INFINITY;
+#pragma unroll
+      for (int sp = 0; sp < DT_MAX_SPLIT; ++sp) {
+        if (sp < p.split) {
+          const float* ps = part + ((size_t)sp * G + h) * (D + 2);
+          ms[sp] = rd(ps + D + 1);
+          ls[sp] = rd(ps + D);
+          os[sp] = rd(ps + d);
+        } else {
+          ms[sp] = -INFINITY;
+          ls[sp] = os[sp] = 0.f;
+        }
+        M = fmaxf(M, ms[sp]);
+      }
+      float L = 0.f, O = 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int sp = 0; sp < DT_MAX_SPLIT; ++sp) {
+          const float f = fast_exp2(ms[sp] - M);
+          L += f * ls[sp];
+          O += f * os[sp];
+        }
+      }
+      out[idx] = (bf16)(L > 0.f ? O / L : 0.f);
+    }
+  }
+  if constexpr (UPDATE) {
+    // every workgroup of this (stream, KV head) read the old metadata before
+    // its ticket (or, with one workgroup, before the barrier above)
+    if (tid == 0)
+      commit(tr, c.state + (size_t)bh * 8, c.slot_pos + (size_t)bh * slots, c.slot_sep + (size_t)bh * slots,
+             new_sep, ev_pos, new_oldsep);
+  }
+}
+
+// Tiled path: workgroups per (stream, KV head), 0 if the cache is too large.
+int dt_split(int rows) {
+  const int n_tiles = (rows + DT_ROWS - 1) / DT_ROWS;
+  const int sp = (n_tiles + DT_TPW - 1) / DT_TPW;
+  return sp <= DT_MAX_SPLIT ? sp : 0;
+}
+
+int attend_rows(const sepcache* c, bool update) { return c->a + c->s + c->n + 1 + (update ? 1 : 0); }
+// split path: workgroups per (stream, KV head)
 int attend_split(const sepcache* c, bool update) {
-  if (attend_fused(c, update)) return 1;
   const int per_split = SPLIT_THREADS / (c->d / 8) * SPLIT_MAXR;
   return (attend_rows(c, update) + per_split - 1) / per_split;
 }
 
 template <int D, int G, bool UPDATE, bool SHIFT>
-void launch_attend_t(const AttendParams& p, bool fused, hipStream_t st) {
-  if (fused) {
-    hipLaunchKernelGGL((attend_part<D, G, UPDATE, SHIFT, FUSED_THREADS, FUSED_MAXR, true>),
-                       dim3(p.c.B * p.c.Hkv), dim3(FUSED_THREADS), 0, st, p);
+void launch_attend_t(const AttendParams& p, hipStream_t st) {
+  if (p.tiled) {
+    hipLaunchKernelGGL((decode_tiles<D, G, UPDATE, SHIFT>), dim3(p.c.B * p.c.Hkv * p.split), dim3(DT_THREADS), 0,
+                       st, p);
   } else {
-    hipLaunchKernelGGL((attend_part<D, G, UPDATE, SHIFT, SPLIT_THREADS, SPLIT_MAXR, false>),
-                       dim3(p.c.B * p.c.Hkv * p.split), dim3(SPLIT_THREADS), 0, st, p);
+    hipLaunchKernelGGL((attend_part<D, G, UPDATE, SHIFT>), dim3(p.c.B * p.c.Hkv * p.split), dim3(SPLIT_THREADS), 0,
+                       st, p);
     hipLaunchKernelGGL((attend_merge<D, G, UPDATE>), dim3(p.c.B * p.c.Hkv), dim3(MERGE_THREADS), 0, st, p);
   }
 }
 
 template <int D, int G>
 int launch_attend(const AttendParams& p, bool update, hipStream_t st) {
-  const bool fused = p.split == 1;
   if (update) {
-    if (p.shift) launch_attend_t<D, G, true, true>(p, fused, st);
-    else launch_attend_t<D, G, true, false>(p, fused, st);
+    if (p.shift) launch_attend_t<D, G, true, true>(p, st);
+    else launch_attend_t<D, G, true, false>(p, st);
   } else {
-    if (p.shift) launch_attend_t<D, G, false, true>(p, fused, st);
-    else launch_attend_t<D, G, false, false>(p, fused, st);
+    if (p.shift) launch_attend_t<D, G, false, true>(p, st);
+    else launch_attend_t<D, G, false, false>(p, st);
   }
   return sepattn_hip_check(hipGetLastError(), update ? "step launch" : "decode launch");
 }
@@ -662,13 +1203,16 @@ AttendParams attend_params(const sepcache* c, int Hq, const void* q, float scale
   p.c = make_params(c);
   p.q = (const bf16*)q; p.o = (bf16*)o;
   p.k_new = p.v_new = nullptr; p.is_sep = nullptr;
-  p.part = (float*)ws;
   p.Hq = Hq; p.shift = shift;
-  p.split = attend_split(c, update);
+  const int sp = dt_split(attend_rows(c, update));
+  p.tiled = sp > 0;
+  p.split = p.tiled ? sp : attend_split(c, update);
+  // both paths keep the tickets' area, so one workspace serves either
+  p.part = (float*)ws;
+  if (!p.tiled && ws) p.part = (float*)((char*)ws + dt_ticket_bytes(c->B * c->Hkv));
   p.scale_log2 = scale * 1.4426950408889634f;
-  const double two_pi = 6.283185307179586476925286766559;
-  for (int i = 0; i < MAX_HALF; ++i)
-    p.rev[i] = i < c->d / 2 ? pow((double)c->theta, -2.0 * i / c->d) / two_pi : 0.0;
+  const RopeFreqs f = rope_freqs(c);
+  for (int i = 0; i < MAX_HALF; ++i) p.rev[i] = f.rev[i];
   return p;
 }
 
@@ -687,9 +1231,18 @@ int sepcache_launch_update(const sepcache* c, const void* k_new, const void* v_n
 }
 
 size_t sepcache_decode_ws_bytes(const sepcache* c, int Hq) {
-  const int split = attend_split(c, true);  // the larger of the two
-  if (split == 1 && attend_split(c, false) == 1) return 0;
-  return (size_t)c->B * c->Hkv * split * (Hq / c->Hkv) * (c->d + 2) * 4;
+  const size_t BH = (size_t)c->B * c->Hkv, G = Hq / c->Hkv;
+  size_t need = 0;
+  for (int update = 0; update < 2; ++update) {
+    const int rows = attend_rows(c, update);
+    const int sp = dt_split(rows);
+    size_t b;
+    if (sp == 1) b = 0;
+    else if (sp > 1) b = dt_ticket_bytes((int)BH) + BH * sp * G * (c->d + 2) * 4;
+    else b = dt_ticket_bytes((int)BH) + BH * attend_split(c, update) * G * (c->d + 2) * 4;
+    need = need > b ? need : b;
+  }
+  return need;
 }
 
 int sepcache_launch_decode(const sepcache* c, int Hq, const void* q, float scale, int shift, void* o, void* ws,
