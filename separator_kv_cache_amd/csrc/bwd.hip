@@ -303,6 +303,14 @@ __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
   const int group = p.Hq / p.Hkv;
   const int n_rb = (row_end - j_first + RB - 1) / RB;
   const int n_it = n_rb * group;
+  // Anchor tiles walk their row blocks last to first.  They all end at row
+  // L, so the anchor tiles of one (sequence, KV head), which run together on
+  // one XCD, read the same rows at the same time and share them in L2;
+  // walking up from their different first keys they would share none.
+  // (The band tiles' ranges are staggered at both ends, so their order does
+  // not change what they share.)
+  const int rs_first = anchors ? j_first + RB * (n_rb - 1) : j_first;
+  const int rs_step = anchors ? -RB : RB;
 
   // ---- Q/dO row tiles: global -> registers -> LDS.  Thread x moves chunk
   // x % CH of rows x / CH + u * (NT / CH); rows past L load as zeros and get
@@ -312,13 +320,13 @@ __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
   bool lse_ok = false;
   // fetch() is called for it = 0, 1, 2, ... in order: (row block, head) of
   // the next call advance as counters instead of divisions.
-  int f_rs = j_first, f_h = kvh * group;
+  int f_rs = rs_first, f_h = kvh * group;
   auto fetch = [&](int it) {
     // (uniform values; readfirstlane keeps the buffer resources in scalar
     // registers, else each load becomes a loop over distinct descriptors)
     const int rs = __builtin_amdgcn_readfirstlane(f_rs), h = __builtin_amdgcn_readfirstlane(f_h);
     const bool live = it < n_it;
-    if (++f_h == (kvh + 1) * group) { f_h = kvh * group; f_rs += RB; }
+    if (++f_h == (kvh + 1) * group) { f_h = kvh * group; f_rs += rs_step; }
     const rsrc_t qrs = make_rsrc(p.q + b * p.sq[0] + h * p.sq[1], p.q_span);
     const rsrc_t drs = make_rsrc(p.dout + b * p.so[0] + h * p.so[1], p.o_span);
     const uint32_t qrow = (uint32_t)(p.sq[2] * 2), orow = (uint32_t)(p.so[2] * 2);
@@ -375,11 +383,11 @@ __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
   // transposing read puts in A slot s), so within each 16-row chunk the rows
   // are stored as 0-3, 8-11, 4-7, 12-15 and a lane reads its 8 values at
   // position 16c + 8 hh with one 16-byte read.
-  int a_rs = j_first, a_h = 0;  // row block of the next phase_a call (called for it = 0, 1, ...)
+  int a_rs = rs_first, a_h = 0;  // row block of the next phase_a call (called for it = 0, 1, ...)
   auto phase_a = [&](int it) {
     const char* buf = smem + tbuf(it);
     const int rs = a_rs;
-    if (++a_h == group) { a_h = 0; a_rs += RB; }
+    if (++a_h == group) { a_h = 0; a_rs += rs_step; }
     constexpr int NS = 2 * NKK, PD = 4;
     const char* base = buf + ((32 * hf + qn) * STR + hh * 8) * 2;
     auto opnd = [&](int i) -> bf16x8 {
