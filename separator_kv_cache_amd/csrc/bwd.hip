@@ -236,9 +236,20 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
 // there; tile it - 1 was last read by the second half's B(it - 1), one
 // interval earlier.
 
+// Q/dO tiles of dK/dV are read by rows (16 lanes, one 16-byte chunk of 16
+// consecutive rows) and by transposing reads (32 lanes, 8 bytes of 4
+// consecutive rows each, 64 bytes per row).  At d = 128 the row stride is
+// 160 elements, which keeps the transposing reads' four rows in distinct
+// banks, and chunk c of row r sits at chunk position c ^ ((r >> 2) & 3),
+// which spreads the 16 rows of a row read over all banks as well.  The XOR
+// only touches the low two bits of the chunk index, so a lane's addresses
+// are two precomputed bases plus immediates.  At d = 64 the stride is padded
+// instead.
 template <int D>
 struct DkvLayout {
-  static constexpr int STR = dual_read_stride<D>();           // Q/dO row stride (elements)
+  static constexpr bool SWZ = D == 128;
+  static constexpr int STR = SWZ ? 160 : dual_read_stride<D>();  // Q/dO row stride (elements)
+  __device__ static int tau(int r) { return SWZ ? (r >> 2) & 3 : 0; }
   static constexpr int T_BYTES = RB * STR * 2;                // one Q or dO tile
   static constexpr int BUF_BYTES = 2 * T_BYTES + 2 * RB * 4;  // Q, dO, lse2, D
   static constexpr int PSTR = RB + 8;                         // P/dS: row stride per key (elements)
@@ -355,8 +366,9 @@ __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int r = (int)threadIdx.x / CH + u * (NT / CH), c = (int)threadIdx.x % CH;
-      st16(buf + (r * STR + c * 8) * 2, qr[u]);
-      st16(buf + LY::T_BYTES + (r * STR + c * 8) * 2, dr[u]);
+      const int at = r * STR * 2 + (c ^ LY::tau(r)) * 16;
+      st16(buf + at, qr[u]);
+      st16(buf + LY::T_BYTES + at, dr[u]);
     }
     if (threadIdx.x < RB) {
       float* ls = (float*)(buf + 2 * LY::T_BYTES);
@@ -389,9 +401,15 @@ __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
     const int rs = a_rs;
     if (++a_h == group) { a_h = 0; a_rs += rs_step; }
     constexpr int NS = 2 * NKK, PD = 4;
-    const char* base = buf + ((32 * hf + qn) * STR + hh * 8) * 2;
+    // row 32 hf + qn, chunk c = 2 (i >> 1) + hh at position
+    // 4 (c >> 2) + ((c & 3) ^ tau): two bases, by bit 1 of c
+    const char* row = buf + (32 * hf + qn) * STR * 2;
+    const int ta = LY::tau(32 * hf + qn);
+    const char* base0 = row + ((hh ^ ta) * 16);
+    const char* base1 = row + (((2 + hh) ^ ta) * 16);
     auto opnd = [&](int i) -> bf16x8 {
-      return *(const bf16x8*)(base + ((i & 1) ? LY::T_BYTES : 0) + (i >> 1) * 32);
+      const int k = i >> 1;
+      return *(const bf16x8*)(((k & 1) ? base1 : base0) + ((i & 1) ? LY::T_BYTES : 0) + (k >> 1) * 64);
     };
     f32x16 sacc = f32x16{}, dpacc = f32x16{};
     bf16x8 op[NS];
@@ -447,15 +465,21 @@ __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
   // position 16c + 8(l / 32)); operand reads PD MFMAs ahead.
   auto phase_b = [&](int it) {
     const char* buf = smem + tbuf(it);
-    const char* abase = buf + ((4 * (g >> 1) + (li >> 2)) * STR + HD * hf + 16 * (g & 1) + 4 * (li & 3)) * 2;
+    // row 4 (g >> 1) + (li >> 2) (+ 8 for the upper half, + 16 c), column
+    // HD hf + 16 (g & 1) + 4 (li & 3) (+ 32 db): the chunk's low two bits come
+    // from the lane and are XORed with tau of the row, the rest are immediates
+    const int r0 = 4 * (g >> 1) + (li >> 2);
+    const int clo = 2 * (g & 1) + ((li & 3) >> 1);
+    const char* abase_lo = buf + r0 * STR * 2 + HD * hf * 2 + ((clo ^ LY::tau(r0)) * 16) + 8 * (li & 1);
+    const char* abase_hi = buf + (r0 + 8) * STR * 2 + HD * hf * 2 + ((clo ^ LY::tau(r0 + 8)) * 16) + 8 * (li & 1);
     const char* pb = xp + ((kg * 32 + qn) * PSTR + 8 * hh) * 2;
     const char* sb = xd + ((kg * 32 + qn) * PSTR + 8 * hh) * 2;
     constexpr int NB = (RB / 16) * NDBH * 2, PD = 4;  // MFMA i: chunk c, block db, dV (even) / dK (odd)
     auto opnd = [&](int i) -> bf16x8 {
       const int c = i / (2 * NDBH), db = (i >> 1) % NDBH;
       const int off = ((i & 1) ? 0 : LY::T_BYTES) + (16 * c * STR + 32 * db) * 2;  // dO for dV, Q for dK
-      const bf16x4 lo4 = lds_read_tr16(abase + off);
-      const bf16x4 hi4 = lds_read_tr16(abase + off + 8 * STR * 2);
+      const bf16x4 lo4 = lds_read_tr16(abase_lo + off);
+      const bf16x4 hi4 = lds_read_tr16(abase_hi + off);
       return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
     };
     auto bop = [&](int i) -> bf16x8 {
