@@ -162,6 +162,38 @@ def cpu_baseline(leg: PrefillLeg, budget_s: float = 20.0):
                       f"({kept} kept pairs, {dt:.1f} s)"}
 
 
+def kernel_sources_sha256() -> str:
+    """sha256 over the kernel sources (every file of separator_kv_cache_amd/csrc,
+    by name), to tell whether a stored counter profile still describes them."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "separator_kv_cache_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic() -> dict:
+    """HBM bytes per launch (fetched + written) per kernel from the committed
+    counter profile (profiles/hbm_traffic_per_launch.txt: FETCH_SIZE and
+    WRITE_SIZE passes scaled by a device copy's readings).  Empty when the
+    kernel sources changed since the profile was taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_per_launch.txt")
+    if not os.path.exists(path):
+        return {}
+    sha, out = None, {}
+    for line in open(path):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        if f[0] == "sources_sha256":
+            sha = f[1]
+        elif len(f) == 3:
+            out[f[0]] = int(f[1]) + int(f[2])
+    return out if sha == kernel_sources_sha256() else {}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,19 +290,24 @@ def main():
         "roofline": None,
         "rooflines": None,
     }
+    traffic = measured_traffic()
     dec_launch_us = t_dec * 1e3 / (dec.wl.T * args.layers)
     per_launch_bytes = dec.bytes / (dec.wl.T * args.layers)
     r_dec = {"kernel": "decode_tiles (SepCache step: append, evict, attend; one layer, d=128, 4 q heads per KV head)",
              "bound": "hbm", "achieved": round(per_launch_bytes / (dec_launch_us * 1e-6) / 1e9, 1),
              "peak": PEAK_HBM_GBS, "unit": "GB/s",
-             "frac": round(per_launch_bytes / (dec_launch_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None,
+             "frac": round(per_launch_bytes / (dec_launch_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+             "traffic": traffic.get("decode_tiles"),
              "per_launch_bytes": round(per_launch_bytes), "avg_launch_us": round(dec_launch_us, 3)}
     r_fwd = {"kernel": "fwd_pp_kernel (bf16, d=128)", "bound": "mfma", "achieved": round(fwd_tf, 2),
              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-             "traffic": None, "per_launch_flops": pre.fwd_flops, "avg_launch_ms": round(t_fwd, 4)}
+             "traffic": traffic.get("fwd_pp_kernel"), "per_launch_flops": pre.fwd_flops,
+             "avg_launch_ms": round(t_fwd, 4)}
     r_bwd = {"kernel": "dq_kernel + dkdv_kernel (bf16, d=128)", "bound": "mfma", "achieved": round(bwd_tf, 2),
              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-             "traffic": None, "per_launch_flops": pre.bwd_flops, "avg_launch_ms": round(t_bwd, 4)}
+             "traffic": (traffic["dq_kernel"] + traffic["dkdv_kernel"]
+                         if "dq_kernel" in traffic and "dkdv_kernel" in traffic else None),
+             "per_launch_flops": pre.bwd_flops, "avg_launch_ms": round(t_bwd, 4)}
     # the kernel that dominates a step's time carries the headline roofline
     out["roofline"] = r_dec if t_dec > pre_ms else r_fwd
     out["rooflines"] = [r_fwd, r_bwd, r_dec]
