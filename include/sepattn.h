@@ -212,7 +212,7 @@ SEPATTN_API int sepcache_push(const sepcache* c, const void* k_new, const void* 
  * fp32 for ranks.  The cache is only read.
  * Caches with at most 1024 rows (a + s + n + 1, plus the appended token's row
  * for sepcache_step) run as one kernel: the rows are shared by
- * ceil(rows / 256) workgroups per (stream, KV head), and with more than one
+ * ceil(rows / 512) workgroups per (stream, KV head), and with more than one
  * the last to finish merges the others' partial results from the workspace.
  * There the rotated keys and query enter the score product as bf16 and the
  * probabilities enter P V as bf16, both with fp32 sums.  Larger caches split

@@ -244,6 +244,7 @@ struct AttendParams {
   float* part;  // workspace: partial results (and, tiled path, tickets)
   int Hq, shift, split, tiled;
   float scale_log2;
+  float rev_log2_step;   // -2 log2(theta) / d: frequency i turns 2^(i * step) / (2 pi) per position
   double rev[MAX_HALF];  // theta^(-2i/d) / (2 pi): RoPE revolutions per position
 };
 
@@ -604,10 +605,9 @@ __global__ __launch_bounds__(MERGE_THREADS) void attend_merge(AttendParams p) {
 
 // ---- tiled path
 //
-// Workgroups of 8 waves; the rows of one (stream, KV head) are cut into
+// Workgroups of 16 waves; the rows of one (stream, KV head) are cut into
 // tiles of 16, held by one workgroup of at most DT_TPW tiles or shared by
-// several (larger caches); every wave takes up to three tiles, eight apart.
-// Per tile:
+// two (larger caches).  Per tile:
 //  * scores S = K Q^T on 16x16x32 bf16 MFMAs, keys along the rows: lane
 //    (g, col) (g = lane / 16) loads row 16t + col, dimensions 32m + 8g .. +7
 //    for m < D/32, so each RoPE pair (i, i + D/2) lies in one lane; query
@@ -616,17 +616,19 @@ __global__ __launch_bounds__(MERGE_THREADS) void attend_merge(AttendParams p) {
 //  * O += P V on 16x16x16 bf16 MFMAs: lane (g, c) loads rows 16t + 4g .. +3,
 //    dimensions 8c .. 8c+7 and transposes that 4x8 block in registers, so
 //    MFMA e takes dimension 8c + e of each column c.
-// K/V addresses are physical rows, so no load waits for the counters.  A
-// wave requests its first tile once the counters and query have arrived
-// (loads queue in order, so those small ones would otherwise wait behind
-// the rows) and each later one just before scoring the previous: a compute
-// unit keeps only so many loads in flight, and a wave blocked on issuing one
-// could not compute meanwhile.  A wave keeps
-// the scores of its tiles and takes one maximum over them; the waves'
-// (o, sum, max) merge through LDS.  With several workgroups per (stream, KV
-// head), each writes that triple to the workspace and the last to arrive
-// (an atomic ticket per (stream, KV head), reset by that workgroup) merges
-// them, writes o and, for a step, commits the slot metadata.
+// K/V addresses are physical rows, so every wave issues all its loads right
+// after one barrier at entry.  The counters and the row intervals that
+// follow from them are computed once, by wave 0, which holds no tile unless
+// the others are full; it publishes them in LDS behind a flag that the
+// other waves poll.  No barrier sits between the loads and the scores: a
+// compute unit keeps only so many loads in flight, so waves that are still
+// blocked issuing theirs would hold back those whose data has arrived.  A
+// wave keeps the scores of its tiles and takes one maximum over them; the
+// waves' (o, sum, max) merge through LDS after the one barrier at the end.
+// With two workgroups per (stream, KV head), each writes that triple to the
+// workspace and the last to arrive (an atomic ticket per (stream, KV head),
+// reset by that workgroup) merges them, writes o and, for a step, commits
+// the slot metadata.
 //
 // RoPE with positions shifted to ranks.  A row's rank is its physical index
 // plus an offset that is constant on a few intervals of rows: the sinks, the
@@ -635,41 +637,37 @@ __global__ __launch_bounds__(MERGE_THREADS) void attend_merge(AttendParams p) {
 // compose, so for row 16t + col of interval k, with rank 16t + col + delta_k,
 //     R(rank) k . R(p_q) q  =  R(col) k . R(p_q - delta_k - 16t) q.
 // Keys turn by their column's angle (a 16-row table in LDS, so a lane's angles
-// are the same for all its tiles) and each (interval, tile) pair gets its own
-// copy of the query turned by the rest, built once per workgroup in LDS.  A
-// tile that meets several intervals runs its score MFMAs once per interval
-// and keeps each row's own result.  With original positions, keys turn by
-// their own angle and the query is one copy.
+// are the same for all its tiles) and the query by the rest: a wave turns
+// its own copy of the query for each (interval, tile) pair it scores, into
+// its slice of LDS.  A tile that meets several intervals runs its score
+// MFMAs once per interval and keeps each row's own result.  With original
+// positions, keys turn by their own angle and the query is one copy.
 //
 // Rows that hold no entry get probability zero; a non-finite value in such a
 // slot would still reach the output through 0 * V in the MFMA, so
 // sepcache_reset zeroes every slot and slots only receive tokens' K and V.
 
-constexpr int DT_WAVES = 8;
+constexpr int DT_WAVES = 16;
 constexpr int DT_THREADS = 64 * DT_WAVES;
 constexpr int DT_ROWS = 16;   // rows per tile
-constexpr int DT_MAXT = 3;    // tiles per wave
+constexpr int DT_MAXT = 2;    // tiles per wave
 constexpr int DT_TPW = DT_WAVES * DT_MAXT;  // tiles per workgroup
-constexpr int DT_MAX_SPLIT = 4;
+constexpr int DT_MAX_SPLIT = 2;
 constexpr int DT_MAX_ROWS = DT_MAX_SPLIT * DT_TPW * DT_ROWS;
 constexpr int DT_NCLS = 7;    // intervals of constant rank offset
-constexpr int DT_MAX_VAR = DT_TPW + DT_NCLS - 1;  // (interval, tile) pairs of one workgroup
 constexpr size_t DT_TICKET_BYTES = 256;            // per 64 (stream, KV head) pairs
 
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // Row intervals [lo, hi) of constant rank - row = delta; a row of interval k
-// holds an entry iff its rank lies in [vlo, vhi).  The (interval, tile) pairs
-// of tiles [t_lo, t_hi) are numbered interval by interval: interval k meets
-// tiles t0 .. and its pairs start at first.
+// holds an entry iff its rank lies in [vlo, vhi).
 struct RowClasses {
   int lo[DT_NCLS], hi[DT_NCLS], delta[DT_NCLS], vlo[DT_NCLS], vhi[DT_NCLS];
-  int first[DT_NCLS], t0[DT_NCLS], n_var;
 };
 
 template <bool UPDATE>
 __device__ __forceinline__ RowClasses row_classes(const Counters& c0, const Transition& tr, int a, int s, int n,
-                                                  int slots, int t_lo, int t_hi) {
+                                                  int slots) {
   const Counters& c1 = tr.after;
   const int drop = tr.sep_drop ? 1 : 0, ev = tr.evicted ? 1 : 0;
   const int sep0 = a + c0.seph, win0 = a + s + c0.winh;
@@ -687,7 +685,6 @@ __device__ __forceinline__ RowClasses row_classes(const Counters& c0, const Tran
   const int vl[DT_NCLS] = {0, sep_rank, sep_rank, win_rank, win_rank, win_rank - 1, total - 1};
   const int vh[DT_NCLS] = {c0.nsink, sep_rank + c0.sepc - drop, sep_rank + c0.sepc - drop,
                            win_rank + c0.winc - ev, win_rank + c0.winc - ev, win_rank, total};
-  int nv = 0;
 #pragma unroll
   for (int k = 0; k < DT_NCLS; ++k) {
     rc.lo[k] = lo[k];
@@ -695,21 +692,8 @@ __device__ __forceinline__ RowClasses row_classes(const Counters& c0, const Tran
     rc.delta[k] = dl[k];
     rc.vlo[k] = vl[k];
     rc.vhi[k] = vh[k];
-    rc.first[k] = nv;
-    const int a0 = max(lo[k] / DT_ROWS, t_lo), a1 = min((hi[k] - 1) / DT_ROWS, t_hi - 1);
-    rc.t0[k] = a0;
-    if (hi[k] > lo[k] && a1 >= a0) nv += a1 - a0 + 1;
   }
-  rc.n_var = nv;
   return rc;
-}
-
-// Bits of the rows of tile [row0, row0 + 16) that belong to interval k and
-// hold an entry (wave-uniform).
-__device__ __forceinline__ uint32_t class_rows(const RowClasses& rc, int k, int row0) {
-  const int lo = max(max(rc.lo[k], rc.vlo[k] - rc.delta[k]), row0) - row0;
-  const int hi = min(min(rc.hi[k], rc.vhi[k] - rc.delta[k]), row0 + DT_ROWS) - row0;
-  return hi > lo ? ((1u << hi) - 1u) & ~((1u << lo) - 1u) : 0u;
 }
 
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
@@ -740,14 +724,21 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
   constexpr int NP = NM / 2;  // chunks m < NP pair with m + NP
   constexpr int NCH = D / 8;  // 16-byte chunks per row
   constexpr int HALF = D / 2;
-  constexpr int NQ = SHIFT ? DT_MAX_VAR : 1;  // query copies
-  constexpr int QSTR = D + 8;                 // LDS row of one (copy, head); the pad spreads banks
-  constexpr int TSTR = HALF + 2;              // LDS row of the column angles, likewise
-  __shared__ __attribute__((aligned(16))) bf16 qvar[NQ * G * QSTR];
+  constexpr int QSTR = D + 8;  // LDS row of one head of a query copy; the pad spreads banks
+  constexpr int TSTR = HALF + 2;  // LDS row of the column angles, likewise
+  // each wave's query copy and output (apart, so that a wave writes its
+  // output while others still score)
+  __shared__ __attribute__((aligned(16))) bf16 qc_all[DT_WAVES * G * QSTR];
+  __shared__ __attribute__((aligned(16))) float o_w[DT_WAVES][G][D];
   __shared__ __attribute__((aligned(16))) float2 tcol[SHIFT ? DT_ROWS * TSTR : 1];
-  __shared__ float o_w[DT_WAVES][G][D];
+  __shared__ __attribute__((aligned(16))) u32x4 newrow[2][NCH];  // appended token's K and V (step)
   __shared__ float m_w[DT_WAVES][G], l_w[DT_WAVES][G];
-  __shared__ int last_s;
+  // published by wave 0: per interval, the rows [x, y) that hold an entry and
+  // rank - row (z); then the query position and the rows that move
+  __shared__ __attribute__((aligned(16))) int4 cls_tab[8];
+  __shared__ int info[4];
+  __shared__ double rev_lds[SHIFT ? 1 : HALF];
+  __shared__ int ready, last_s;
 
   const CacheParams& c = p.c;
   const int BH = c.B * c.Hkv;
@@ -764,63 +755,59 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
   const uint32_t row_bytes = D * 2;
   bf16* kb = c.k + (size_t)bh * slots * D;
   bf16* vb = c.v + (size_t)bh * slots * D;
+  const bool lead = wave == 0;
 
-  // ---- loads independent of the counters.  Everything the prologue needs
-  // per lane is requested before the K/V rows, so that waiting for it never
-  // waits for them.
-  const int32_t* st = c.state + (size_t)bh * 8;
-  Counters c0;
-  c0.t = __builtin_amdgcn_readfirstlane(st[ST_T]);
-  c0.nsink = __builtin_amdgcn_readfirstlane(st[ST_NSINK]);
-  c0.seph = __builtin_amdgcn_readfirstlane(st[ST_SEPH]);
-  c0.sepc = __builtin_amdgcn_readfirstlane(st[ST_SEPC]);
-  c0.winh = __builtin_amdgcn_readfirstlane(st[ST_WINH]);
-  c0.winc = __builtin_amdgcn_readfirstlane(st[ST_WINC]);
-  c0.flags = __builtin_amdgcn_readfirstlane(st[ST_FLAGS]);
-  c0.oldsep = __builtin_amdgcn_readfirstlane(st[ST_OLDSEP]);
+  // ---- the counters (lane i: word i) and the separator flag go out first,
+  // as vector loads: a scalar load would be waited for by every later wait
+  // on a kernel argument or an LDS access
+  // (every wave issues them, so that no load is conditional: the waits on
+  // the loads after them stay counted)
+  const int st_l = bld4(make_rsrc(c.state + (size_t)bh * 8, 32), lane < 8 ? (uint32_t)lane * 4u : BUF_OOB);
   const int is_sep_b = UPDATE ? (int)p.is_sep[b] : 0;
-  // the query pair this thread turns in the prologue: dims i and i + D/2 of
-  // copies tid / HALF, tid / HALF + DT_THREADS / HALF, ...
-  const int qi = tid % HALF;
-  const double rev_q = p.rev[qi];
-  float qx1[G], qx2[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const bf16* qr = p.q + ((size_t)b * p.Hq + kvh * G + h) * D;
-    qx1[h] = bf2f(qr[qi]);
-    qx2[h] = bf2f(qr[qi + HALF]);
+  if (tid == 0) ready = 0;
+  // the column angles (shifted positions): no memory involved
+  if constexpr (SHIFT) {
+    for (int idx = tid; idx < DT_ROWS * HALF; idx += DT_THREADS) {
+      const int i = idx % HALF;
+      float cs, sn;
+      rope_cs<true>(idx / HALF, 0.0, fast_exp2((float)i * p.rev_log2_step) * 0.15915494309189535f, cs, sn);
+      tcol[(idx / HALF) * TSTR + i] = make_float2(cs, sn);
+    }
   }
-  // original positions: this lane's key frequencies i = 32 m + 8 g + e, m < NP
-  double rev_k[SHIFT ? 1 : NP][8];
-  if constexpr (!SHIFT) {
-#pragma unroll
-    for (int m = 0; m < NP; ++m)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) rev_k[m][e] = p.rev[32 * m + 8 * g + e];
-  }
+  // the only barrier before the merge (the waves start together).  A bare
+  // barrier after an LDS-only wait: __syncthreads' fence would also wait for
+  // the loads just issued.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // wave w takes tiles t_hi-1-w and t_hi-9-w: in a step the last tile, which
-  // holds the appended token's row, is wave 0's first in the last workgroup
+  // ---- loads: the query (lane l < D/2: dimensions 2l, 2l + 1 of each head,
+  // so that lane l ^ D/4 holds their RoPE partners), its frequencies, then the
+  // K/V tiles.  Tiles go, from the last down, to waves 1, 2, ..., 15 in
+  // turn, and to wave 0, which does the counters, only once those are full.
+  // In a step the last tile, which holds the appended token's row, is wave
+  // 1's first in the last workgroup; wave 1 stages that row through LDS, one
+  // 16-byte chunk per lane.
+  constexpr int QL = HALF / 2;
+  uint32_t q_own[G];
+  {
+    const rsrc_t qrs = make_rsrc(p.q + ((size_t)b * p.Hq + kvh * G) * D, G * D * 2);
+#pragma unroll
+    for (int h = 0; h < G; ++h) q_own[h] = (uint32_t)bld4(qrs, lane < HALF ? (uint32_t)(h * D + 2 * lane) * 2u : BUF_OOB);
+  }
+  const int fi = 2 * (lane % QL);  // this lane's frequencies fi, fi + 1
+  const double rv0 = p.rev[fi], rv1 = p.rev[fi + 1];
   auto tile_of = [&](int j) {
-    const int t = t_hi - 1 - wave - DT_WAVES * j;
+    const int k = lead ? (DT_WAVES - 1) * DT_MAXT + j : (DT_WAVES - 1) * j + wave - 1;
+    const int t = t_hi - 1 - k;
     return t >= t_lo ? t : -1;
   };
-  // The appended token's row first (step): rows past the cache read as zeros
-  // below and these loads fill row `slots`.  Every tile load is issued
-  // unconditionally (absent tiles at an offset past the end, which reads
-  // zeros and touches no memory), so that each wait counts exactly the loads
-  // issued after the ones it needs.
-  const bool holds_new = UPDATE && wave == 0 && t_hi == n_tiles;
-  u32x4 kin[NM], vin[4];
+  const bool holds_new = UPDATE && wave == 1 && t_hi == n_tiles;
+  u32x4 nk, nv;
   if (holds_new) {
-    const int krow = (n_tiles - 1) * DT_ROWS + col;
-    const rsrc_t kis = make_rsrc(p.k_new + (size_t)bh * D, row_bytes);
-    const rsrc_t vis = make_rsrc(p.v_new + (size_t)bh * D, row_bytes);
-#pragma unroll
-    for (int m = 0; m < NM; ++m) kin[m] = bld16(kis, krow == slots ? (4 * m + g) * 16 : BUF_OOB);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      vin[u] = bld16(vis, ((n_tiles - 1) * DT_ROWS + 4 * g + u == slots && col < NCH) ? col * 16 : BUF_OOB);
+    nk = bld16(make_rsrc(p.k_new + (size_t)bh * D, row_bytes), lane < NCH ? lane * 16 : BUF_OOB);
+    nv = bld16(make_rsrc(p.v_new + (size_t)bh * D, row_bytes), lane >= 32 && lane - 32 < NCH ? (lane - 32) * 16 : BUF_OOB);
   }
   const rsrc_t krs = make_rsrc(kb, (uint32_t)slots * row_bytes);
   const rsrc_t vrs = make_rsrc(vb, (uint32_t)slots * row_bytes);
@@ -830,7 +817,8 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
   // An absent tile (t = -1) sets the offsets' top bit arithmetically rather
   // than by a select, so the compiler neither branches on it nor merges the
   // identical loads it would produce (either would put a wait here).
-  auto issue = [&](int j) {
+#pragma unroll
+  for (int j = 0; j < DT_MAXT; ++j) {
     const int t = tile_of(j);
     const uint32_t absent = (uint32_t)(t >> 31) & BUF_OOB;
     const int krow = t * DT_ROWS + col;
@@ -840,94 +828,127 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
     for (int u = 0; u < 4; ++u)
       vr[j][u] = bld16(vrs, col < NCH ? ((uint32_t)(t * DT_ROWS + 4 * g + u) * row_bytes + col * 16) | absent : BUF_OOB);
     if constexpr (!SHIFT) spos[j] = bld4(prs, ((uint32_t)krow * 4) | absent);
-  };
-  const bool new_sep = __builtin_amdgcn_readfirstlane(is_sep_b) != 0;
-
-  // ---- counters after the step, row intervals, query copies
-  const Transition tr = transition(c0, c.a, c.s, c.n, UPDATE, new_sep, UPDATE);
-  const Counters c1 = tr.after;
-  const int total = c1.nsink + c1.sepc + c1.winc;
-  int ev_pos = -1, new_oldsep = 0;
-  if constexpr (UPDATE) {
-    if (tid == 0) {
-      if (tr.evicted) ev_pos = c.slot_pos[(size_t)bh * slots + tr.ev_src];
-      if (tr.refresh_oldsep) new_oldsep = c.slot_sep[(size_t)bh * slots + c.a + c.s + c1.winh];
-    }
   }
-  const RowClasses rc = row_classes<UPDATE>(c0, tr, c.a, c.s, c.n, slots, t_lo, t_hi);
-  issue(0);  // after the small loads above have arrived, so they did not queue behind it
-  {
-    const float rev32 = (float)rev_q;
-    const int n_copies = SHIFT ? min(rc.n_var, DT_MAX_VAR) : 1;
-    for (int v = tid / HALF; v < n_copies; v += DT_THREADS / HALF) {
-      int pos;
-      if constexpr (SHIFT) {
-        // the interval owning copy v: the last non-empty one starting at or before it
-        int at = 0;
+
+  // ---- wave 0: the counters after the step and the row intervals,
+  // published in LDS
+  // used by the commit only (thread 0, in wave 0): no defaults on the other
+  // waves' path, which would make wave 0 wait here for the loads below
+  int ev_pos, new_oldsep;
+  Transition tr;
+  bool new_sep;
+  if (lead) {
+    if constexpr (!SHIFT) {
+      if (lane < HALF) rev_lds[lane] = p.rev[lane];
+    }
+    Counters c0;
+    c0.t = __builtin_amdgcn_readlane(st_l, ST_T);
+    c0.nsink = __builtin_amdgcn_readlane(st_l, ST_NSINK);
+    c0.seph = __builtin_amdgcn_readlane(st_l, ST_SEPH);
+    c0.sepc = __builtin_amdgcn_readlane(st_l, ST_SEPC);
+    c0.winh = __builtin_amdgcn_readlane(st_l, ST_WINH);
+    c0.winc = __builtin_amdgcn_readlane(st_l, ST_WINC);
+    c0.flags = __builtin_amdgcn_readlane(st_l, ST_FLAGS);
+    c0.oldsep = __builtin_amdgcn_readlane(st_l, ST_OLDSEP);
+    new_sep = __builtin_amdgcn_readfirstlane(is_sep_b) != 0;
+    tr = transition(c0, c.a, c.s, c.n, UPDATE, new_sep, UPDATE);
+    const Counters& c1 = tr.after;
+    const RowClasses rc = row_classes<UPDATE>(c0, tr, c.a, c.s, c.n, slots);
+    if (lane == 0) {
 #pragma unroll
-        for (int k = 0; k < DT_NCLS; ++k)
-          if (rc.hi[k] > rc.lo[k] && v >= rc.first[k]) at = rc.delta[k] + (rc.t0[k] + v - rc.first[k]) * DT_ROWS;
-        pos = total - 1 - at;
-      } else {
-        pos = c1.t - 1;
-      }
-      float cs, sn;
-      rope_cs<SHIFT>(pos, rev_q, rev32, cs, sn);
-      cs *= p.scale_log2;
-      sn *= p.scale_log2;
+      for (int k = 0; k < DT_NCLS; ++k)
+        cls_tab[k] = make_int4(max(rc.lo[k], rc.vlo[k] - rc.delta[k]), min(rc.hi[k], rc.vhi[k] - rc.delta[k]),
+                               rc.delta[k], 0);
+      cls_tab[DT_NCLS] = make_int4(0, 0, 0, 0);
+      // shifted: the query's rank; original positions: its position
+      info[0] = SHIFT ? c1.nsink + c1.sepc + c1.winc - 1 : c1.t - 1;
+      info[1] = UPDATE ? tr.app_slot : -1;
+      info[2] = UPDATE ? tr.ev_src : -1;
+      info[3] = UPDATE ? tr.ev_dst : -1;
+    }
+    // the LDS writes above complete before the flag (an LDS wait only: the
+    // tile loads stay in flight)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    if (lane == 0) __hip_atomic_store(&ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if constexpr (UPDATE) {
+      // read by the commit at the end; vector loads, so nothing here waits for them
+      ev_pos = bld4(prs, tr.evicted ? (uint32_t)tr.ev_src * 4u : BUF_OOB);
+      new_oldsep = (int)__builtin_amdgcn_raw_buffer_load_b8(
+          make_rsrc(c.slot_sep + (size_t)bh * slots, (uint32_t)slots),
+          tr.refresh_oldsep ? (uint32_t)(c.a + c.s + c1.winh) : BUF_OOB, 0, 0);
+    }
+  } else {
+    // wave 0 always sets the flag, so this wait ends
+    while (__hip_atomic_load(&ready, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0) __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int4 ct = cls_tab[lane & 7];  // lanes k < 7: interval k
+  const int q_pos = __builtin_amdgcn_readfirstlane(info[0]);
+  const int app_slot = __builtin_amdgcn_readfirstlane(info[1]);
+  const int ev_src = __builtin_amdgcn_readfirstlane(info[2]);
+  const int ev_dst = __builtin_amdgcn_readfirstlane(info[3]);
+
+  // ---- this wave's query copy: turned to `pos`, scaled into the log2
+  // domain; lane l < D/2 writes dimensions 2l, 2l + 1 of each head.  Lanes
+  // l < D/4 hold the first element x1 of their pairs, lanes D/4 <= l < D/2
+  // the second x2:   y1 = x1 cos - x2 sin,   y2 = x2 cos + x1 sin.
+  bf16* const qc = qc_all + wave * (G * QSTR);
+  uint32_t q_oth[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) q_oth[h] = (uint32_t)__shfl_xor((int)q_own[h], QL, 64);
+  const float sgn = (lane & QL) ? p.scale_log2 : -p.scale_log2;
+  auto build_copy = [&](int pos) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");  // after the previous pass's reads
+    float cs0, sn0, cs1, sn1;
+    rope_cs<SHIFT>(pos, rv0, (float)rv0, cs0, sn0);
+    rope_cs<SHIFT>(pos, rv1, (float)rv1, cs1, sn1);
+    cs0 *= p.scale_log2;
+    cs1 *= p.scale_log2;
+    sn0 *= sgn;
+    sn1 *= sgn;
+    if (lane < HALF)
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        bf16* dst = qvar + (v * G + h) * QSTR;
-        dst[qi] = (bf16)(qx1[h] * cs - qx2[h] * sn);
-        dst[qi + HALF] = (bf16)(qx2[h] * cs + qx1[h] * sn);
+        const float y0 = lo_bf(q_own[h]) * cs0 + lo_bf(q_oth[h]) * sn0;
+        const float y1 = hi_bf(q_own[h]) * cs1 + hi_bf(q_oth[h]) * sn1;
+        *(uint32_t*)(qc + h * QSTR + 2 * lane) = pack_bf(y0, y1);
       }
-    }
-    if constexpr (SHIFT) {
-      for (int idx = tid; idx < DT_ROWS * HALF; idx += DT_THREADS) {  // idx % HALF == qi
-        float cs, sn;
-        rope_cs<true>(idx / HALF, 0.0, rev32, cs, sn);
-        tcol[(idx / HALF) * TSTR + qi] = make_float2(cs, sn);
-      }
-    }
-  }
-  __syncthreads();
+    // read back by this wave only: its LDS accesses complete in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  if constexpr (!SHIFT) build_copy(q_pos);
 
   // this lane's key angles (shifted positions): column col, frequencies
   // i = 32 m + 8 g + e, m < NP
-  float kc[SHIFT ? NP : 1][8], ks[SHIFT ? NP : 1][8];
-  if constexpr (SHIFT) {
-#pragma unroll
-    for (int m = 0; m < NP; ++m)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 v = tcol[col * TSTR + 32 * m + 8 * g + e];
-        kc[m][e] = v.x;
-        ks[m][e] = v.y;
-      }
-  }
+  const float2* kcs = tcol + col * TSTR + 8 * g;
 
   // ---- scores of this wave's tiles
   f32x4 sco[DT_MAXT];
 #pragma unroll
   for (int j = 0; j < DT_MAXT; ++j) {
-    if (j + 1 < DT_MAXT) issue(j + 1);
     const int t = tile_of(j);
     sco[j] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (t < 0) continue;
     const int row0 = t * DT_ROWS;
     const int krow = row0 + col;
-    if (j == 0 && holds_new) {
+    if (j == 0 && holds_new) {  // rows past the cache read as zeros; fill row `slots`
+      if (lane < NCH) newrow[0][lane] = nk;
+      if (lane >= 32 && lane - 32 < NCH) newrow[1][lane - 32] = nv;
+      if (krow == slots)
 #pragma unroll
-      for (int m = 0; m < NM; ++m) kr[0][m] |= kin[m];
+        for (int m = 0; m < NM; ++m) kr[0][m] = newrow[0][4 * m + g];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) vr[0][u] |= vin[u];
+      for (int u = 0; u < 4; ++u)
+        if (row0 + 4 * g + u == slots && col < NCH) vr[0][u] = newrow[1][col];
     }
 
     if constexpr (UPDATE) {  // rows that move: raw K/V to their new slots
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
-        const int src = w == 0 ? slots : tr.ev_src;
-        const int dst = w == 0 ? tr.app_slot : tr.ev_dst;
+        const int src = w == 0 ? slots : ev_src;
+        const int dst = w == 0 ? app_slot : ev_dst;
         if (dst >= 0 && src >= row0 && src < row0 + DT_ROWS) {
           if (krow == src)
 #pragma unroll
@@ -939,62 +960,73 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
       }
     }
 
-    // K turned: pairs (m, e) and (m + NP, e)
+    // K turned: pairs (m, e) and (m + NP, e), packed chunk pair by chunk pair
     bf16x8 ka[NM];
-    {
-      float y[NM][8];
 #pragma unroll
-      for (int m = 0; m < NP; ++m)
+    for (int m = 0; m < NP; ++m) {
+      u32x4 w1o, w2o;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t w1 = kr[j][m][e >> 1], w2 = kr[j][m + NP][e >> 1];
-          const float x1 = (e & 1) ? hi_bf(w1) : lo_bf(w1);
-          const float x2 = (e & 1) ? hi_bf(w2) : lo_bf(w2);
+      for (int q = 0; q < 4; ++q) {
+        float y1[2], y2[2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int e = 2 * q + h2;
+          const uint32_t w1 = kr[j][m][q], w2 = kr[j][m + NP][q];
+          const float x1 = h2 ? hi_bf(w1) : lo_bf(w1);
+          const float x2 = h2 ? hi_bf(w2) : lo_bf(w2);
           float cs, sn;
           if constexpr (SHIFT) {
-            cs = kc[m][e];
-            sn = ks[m][e];
+            const float2 a = kcs[32 * m + e];
+            cs = a.x;
+            sn = a.y;
           } else {
-            const int pos = krow == slots ? c1.t - 1 : spos[j];
-            rope_cs<false>(pos, rev_k[m][e], 0.f, cs, sn);
+            const int pos = krow == slots ? q_pos : spos[j];
+            rope_cs<false>(pos, rev_lds[32 * m + 8 * g + e], 0.f, cs, sn);
           }
-          y[m][e] = x1 * cs - x2 * sn;
-          y[m + NP][e] = x2 * cs + x1 * sn;
+          y1[h2] = x1 * cs - x2 * sn;
+          y2[h2] = x2 * cs + x1 * sn;
         }
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        u32x4 w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = pack_bf(y[m][2 * q], y[m][2 * q + 1]);
-        ka[m] = __builtin_bit_cast(bf16x8, w);
+        w1o[q] = pack_bf(y1[0], y1[1]);
+        w2o[q] = pack_bf(y2[0], y2[1]);
       }
+      ka[m] = __builtin_bit_cast(bf16x8, w1o);
+      ka[m + NP] = __builtin_bit_cast(bf16x8, w2o);
     }
 
-    // one pass per interval the tile meets; each row keeps its own interval's
-    // score, rows that hold no entry keep -inf
+    // the tile's rows per interval (lanes k < 7), one pass per interval it
+    // meets: each row keeps its own interval's score, rows that hold no
+    // entry keep -inf
+    const int lo = max(ct.x, row0) - row0, hi = min(ct.y, row0 + DT_ROWS) - row0;
+    const uint32_t mk = (lane < DT_NCLS && hi > lo) ? (((1u << hi) - 1u) & ~((1u << lo) - 1u)) : 0u;
     f32x4 s = sco[j];
-    uint32_t all = 0;
-#pragma unroll
-    for (int k = 0; k < DT_NCLS; ++k) {
-      uint32_t mk = class_rows(rc, k, row0);
-      if constexpr (!SHIFT) {  // one query copy: a single pass over every kept row
-        all |= mk;
-        if (k < DT_NCLS - 1) continue;
-        mk = all;
-      }
-      if (mk == 0) continue;
-      const int v = SHIFT ? min(rc.first[k] + t - rc.t0[k], DT_MAX_VAR - 1) : 0;
-      const bf16* qv = qvar + (v * G + (col & (G - 1))) * QSTR;
+    auto pass = [&](uint32_t rows_mask) {
+      const bf16* qv = qc + (col & (G - 1)) * QSTR;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
         const bf16x8 qb = *(const bf16x8*)(qv + (4 * m + g) * 8);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[m], qb, acc, 0, 0, 0);
       }
-      const uint32_t mine = mk >> (4 * g);
+      const uint32_t mine = rows_mask >> (4 * g);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if ((mine >> r) & 1u) s[r] = acc[r];
+    };
+    if constexpr (SHIFT) {
+      uint64_t todo = __builtin_amdgcn_ballot_w64(mk != 0);
+      while (todo) {
+        const int k = (int)__builtin_ctzll(todo);
+        todo &= todo - 1;
+        const uint32_t mkk = (uint32_t)__builtin_amdgcn_readlane((int)mk, k);
+        // rank = row + delta_k, so row 16t + col turns by col and the query by the rest
+        build_copy(q_pos - __builtin_amdgcn_readlane(ct.z, k) - row0);
+        pass(mkk);
+      }
+    } else {
+      uint32_t all = 0;
+#pragma unroll
+      for (int k = 0; k < DT_NCLS; ++k) all |= (uint32_t)__builtin_amdgcn_readlane((int)mk, k);
+      if (all) pass(all);
     }
     sco[j] = s;
   }
@@ -1048,21 +1080,24 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
   }
   __syncthreads();
   bf16* out = p.o + ((size_t)b * p.Hq + kvh * G) * D;
+  // (max, sum, o) of output (h, d) over the waves.  The 64 lanes of a wave
+  // hold 64 consecutive d of one head (D >= 64), so lane l computes the
+  // factor of wave l % DT_WAVES once and the others read it.
+  auto merge_waves = [&](int h, int d, float& M, float& L, float& O) {
+    const int wl = lane % DT_WAVES;
+    const float mw = m_w[wl][h];
+    M = group_max<DT_WAVES>(mw);
+    const float f = M == -INFINITY ? 0.f : fast_exp2(mw - M);
+    L = group_sum<DT_WAVES>(f * l_w[wl][h]);
+    O = 0.f;
+#pragma unroll
+    for (int w = 0; w < DT_WAVES; ++w)
+      O += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), w)) * o_w[w][h][d];
+  };
   if (p.split == 1) {
     for (int idx = tid; idx < G * D; idx += DT_THREADS) {
-      const int h = idx / D, d = idx % D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < DT_WAVES; ++w) M = fmaxf(M, m_w[w][h]);
-      float L = 0.f, O = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < DT_WAVES; ++w) {
-          const float f = fast_exp2(m_w[w][h] - M);
-          L += f * l_w[w][h];
-          O += f * o_w[w][h][d];
-        }
-      }
+      float M, L, O;
+      merge_waves(idx / D, idx % D, M, L, O);
       out[idx] = (bf16)(L > 0.f ? O / L : 0.f);
     }
   } else {
@@ -1070,18 +1105,8 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
     float* part = (float*)((char*)p.part + dt_ticket_bytes(BH)) + (size_t)bh * p.split * G * (D + 2);
     for (int idx = tid; idx < G * D; idx += DT_THREADS) {
       const int h = idx / D, d = idx % D;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < DT_WAVES; ++w) M = fmaxf(M, m_w[w][h]);
-      float L = 0.f, O = 0.f;
-      if (M != -INFINITY) {
-#pragma unroll
-        for (int w = 0; w < DT_WAVES; ++w) {
-          const float f = fast_exp2(m_w[w][h] - M);
-          L += f * l_w[w][h];
-          O += f * o_w[w][h][d];
-        }
-      }
+      float M, L, O;
+      merge_waves(h, d, M, L, O);
       // the partials and the ticket are agent-scope atomics: they are
       // performed at the device's coherence point, with no cache-wide
       // write-back or invalidation
@@ -1138,10 +1163,15 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
   }
   if constexpr (UPDATE) {
     // every workgroup of this (stream, KV head) read the old metadata before
-    // its ticket (or, with one workgroup, before the barrier above)
-    if (tid == 0)
+    // its ticket (or, with one workgroup, before the barrier above); thread 0
+    // belongs to wave 0, which holds the step's transition
+    if (tid == 0) {
+      // opaque here, so that the compiler keeps the commit's selects on these
+      // loaded values down here instead of waiting for the loads early
+      asm volatile("" : "+v"(ev_pos), "+v"(new_oldsep));
       commit(tr, c.state + (size_t)bh * 8, c.slot_pos + (size_t)bh * slots, c.slot_sep + (size_t)bh * slots,
              new_sep, ev_pos, new_oldsep);
+    }
   }
 }
 
@@ -1211,6 +1241,7 @@ AttendParams attend_params(const sepcache* c, int Hq, const void* q, float scale
   p.part = (float*)ws;
   if (!p.tiled && ws) p.part = (float*)((char*)ws + dt_ticket_bytes(c->B * c->Hkv));
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.rev_log2_step = (float)(-2.0 * log2((double)c->theta) / c->d);
   const RopeFreqs f = rope_freqs(c);
   for (int i = 0; i < MAX_HALF; ++i) p.rev[i] = f.rev[i];
   return p;

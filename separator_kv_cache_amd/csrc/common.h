@@ -117,6 +117,16 @@ constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8
 constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within 16
 
+// Maximum over aligned groups of N lanes (N = 4, 8 or 16); every lane gets it.
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  x = fmaxf(x, dpp_mov<DPP_XOR1>(x));
+  x = fmaxf(x, dpp_mov<DPP_XOR2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp_mov<DPP_HALF_MIRROR>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp_mov<DPP_MIRROR>(x));
+  return x;
+}
+
 // Sum over aligned groups of N lanes (N = 4, 8 or 16); every lane gets it.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
