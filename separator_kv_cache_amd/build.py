@@ -24,6 +24,9 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# per source: the decode kernel takes its first arguments preloaded into
+# registers by the dispatcher instead of reading them from memory
+EXTRA = {"cache.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def _run(cmd, verbose):
@@ -45,7 +48,7 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-        _run([HIPCC, *FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run([HIPCC, *FLAGS, *EXTRA.get(src, []), *inc, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         return obj
 
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:

@@ -718,8 +718,14 @@ __host__ __device__ inline size_t dt_ticket_bytes(int bh) {
   return ((size_t)bh * 4 + DT_TICKET_BYTES - 1) / DT_TICKET_BYTES * DT_TICKET_BYTES;
 }
 
+// What a wave needs before it issues its loads comes as leading scalar
+// arguments, which the dispatcher preloads into registers (the struct is read
+// from memory): dims0 = B * Hkv | Hkv << 16 | workgroups per pair << 24,
+// dims1 = slots | Hq << 16.
 template <int D, int G, bool UPDATE, bool SHIFT>
-__global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
+__global__ __launch_bounds__(DT_THREADS) void decode_tiles(const int32_t* state, bf16* kc, bf16* vc, const bf16* qg,
+                                                           const uint8_t* is_sep, uint32_t dims0, uint32_t dims1,
+                                                           float rev_log2_step, AttendParams p) {
   constexpr int NM = D / 32;  // score MFMAs per tile (k = 32 dimensions each)
   constexpr int NP = NM / 2;  // chunks m < NP pair with m + NP
   constexpr int NCH = D / 8;  // 16-byte chunks per row
@@ -741,20 +747,21 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
   __shared__ int ready, last_s;
 
   const CacheParams& c = p.c;
-  const int BH = c.B * c.Hkv;
+  const int BH = (int)(dims0 & 0xffffu), Hkv = (int)((dims0 >> 16) & 0xffu), nsplit = (int)(dims0 >> 24);
+  const int Hq = (int)(dims1 >> 16);
   const int bh = blockIdx.x % BH, split = blockIdx.x / BH;  // splits of one pair are BH apart
-  const int b = bh / c.Hkv, kvh = bh % c.Hkv;
+  const int b = bh / Hkv, kvh = bh % Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile branches stay scalar
   const int g = lane >> 4, col = lane & 15;
-  const int slots = c.slots;
+  const int slots = (int)(dims1 & 0xffffu);
   const int rows = slots + (UPDATE ? 1 : 0);
   const int n_tiles = (rows + DT_ROWS - 1) / DT_ROWS;
-  const int tps = (n_tiles + p.split - 1) / p.split;
+  const int tps = (n_tiles + nsplit - 1) / nsplit;
   const int t_lo = split * tps, t_hi = min(t_lo + tps, n_tiles);  // this workgroup's tiles
   const uint32_t row_bytes = D * 2;
-  bf16* kb = c.k + (size_t)bh * slots * D;
-  bf16* vb = c.v + (size_t)bh * slots * D;
+  bf16* kb = kc + (size_t)bh * slots * D;
+  bf16* vb = vc + (size_t)bh * slots * D;
   const bool lead = wave == 0;
 
   // ---- the counters (lane i: word i) and the separator flag go out first,
@@ -762,15 +769,15 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
   // on a kernel argument or an LDS access
   // (every wave issues them, so that no load is conditional: the waits on
   // the loads after them stay counted)
-  const int st_l = bld4(make_rsrc(c.state + (size_t)bh * 8, 32), lane < 8 ? (uint32_t)lane * 4u : BUF_OOB);
-  const int is_sep_b = UPDATE ? (int)p.is_sep[b] : 0;
+  const int st_l = bld4(make_rsrc(state + (size_t)bh * 8, 32), lane < 8 ? (uint32_t)lane * 4u : BUF_OOB);
+  const int is_sep_b = UPDATE ? (int)is_sep[b] : 0;
   if (tid == 0) ready = 0;
   // the column angles (shifted positions): no memory involved
   if constexpr (SHIFT) {
     for (int idx = tid; idx < DT_ROWS * HALF; idx += DT_THREADS) {
       const int i = idx % HALF;
       float cs, sn;
-      rope_cs<true>(idx / HALF, 0.0, fast_exp2((float)i * p.rev_log2_step) * 0.15915494309189535f, cs, sn);
+      rope_cs<true>(idx / HALF, 0.0, fast_exp2((float)i * rev_log2_step) * 0.15915494309189535f, cs, sn);
       tcol[(idx / HALF) * TSTR + i] = make_float2(cs, sn);
     }
   }
@@ -792,7 +799,7 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
   constexpr int QL = HALF / 2;
   uint32_t q_own[G];
   {
-    const rsrc_t qrs = make_rsrc(p.q + ((size_t)b * p.Hq + kvh * G) * D, G * D * 2);
+    const rsrc_t qrs = make_rsrc(qg + ((size_t)b * Hq + kvh * G) * D, G * D * 2);
 #pragma unroll
     for (int h = 0; h < G; ++h) q_own[h] = (uint32_t)bld4(qrs, lane < HALF ? (uint32_t)(h * D + 2 * lane) * 2u : BUF_OOB);
   }
@@ -805,10 +812,6 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
   };
   const bool holds_new = UPDATE && wave == 1 && t_hi == n_tiles;
   u32x4 nk, nv;
-  if (holds_new) {
-    nk = bld16(make_rsrc(p.k_new + (size_t)bh * D, row_bytes), lane < NCH ? lane * 16 : BUF_OOB);
-    nv = bld16(make_rsrc(p.v_new + (size_t)bh * D, row_bytes), lane >= 32 && lane - 32 < NCH ? (lane - 32) * 16 : BUF_OOB);
-  }
   const rsrc_t krs = make_rsrc(kb, (uint32_t)slots * row_bytes);
   const rsrc_t vrs = make_rsrc(vb, (uint32_t)slots * row_bytes);
   const rsrc_t prs = make_rsrc(c.slot_pos + (size_t)bh * slots, (uint32_t)slots * 4);
@@ -828,6 +831,12 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
     for (int u = 0; u < 4; ++u)
       vr[j][u] = bld16(vrs, col < NCH ? ((uint32_t)(t * DT_ROWS + 4 * g + u) * row_bytes + col * 16) | absent : BUF_OOB);
     if constexpr (!SHIFT) spos[j] = bld4(prs, ((uint32_t)krow * 4) | absent);
+    // after the first tile's loads: its pointers come from the struct
+    if (j == 0 && holds_new) {
+      nk = bld16(make_rsrc(p.k_new + (size_t)bh * D, row_bytes), lane < NCH ? lane * 16 : BUF_OOB);
+      nv = bld16(make_rsrc(p.v_new + (size_t)bh * D, row_bytes),
+                 lane >= 32 && lane - 32 < NCH ? (lane - 32) * 16 : BUF_OOB);
+    }
   }
 
   // ---- wave 0: the counters after the step and the row intervals,
@@ -1079,7 +1088,7 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
     l_w[wave][col] = lsum;
   }
   __syncthreads();
-  bf16* out = p.o + ((size_t)b * p.Hq + kvh * G) * D;
+  bf16* out = p.o + ((size_t)b * Hq + kvh * G) * D;
   // (max, sum, o) of output (h, d) over the waves.  The 64 lanes of a wave
   // hold 64 consecutive d of one head (D >= 64), so lane l computes the
   // factor of wave l % DT_WAVES once and the others read it.
@@ -1094,7 +1103,7 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
     for (int w = 0; w < DT_WAVES; ++w)
       O += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, f), w)) * o_w[w][h][d];
   };
-  if (p.split == 1) {
+  if (nsplit == 1) {
     for (int idx = tid; idx < G * D; idx += DT_THREADS) {
       float M, L, O;
       merge_waves(idx / D, idx % D, M, L, O);
@@ -1102,7 +1111,7 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
     }
   } else {
     int* ticket = (int*)p.part;
-    float* part = (float*)((char*)p.part + dt_ticket_bytes(BH)) + (size_t)bh * p.split * G * (D + 2);
+    float* part = (float*)((char*)p.part + dt_ticket_bytes(BH)) + (size_t)bh * nsplit * G * (D + 2);
     for (int idx = tid; idx < G * D; idx += DT_THREADS) {
       const int h = idx / D, d = idx % D;
       float M, L, O;
@@ -1125,7 +1134,7 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
     __syncthreads();
     if (tid == 0) {
       const int seen = __hip_atomic_fetch_add(ticket + bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int last = seen == p.split - 1;
+      const int last = seen == nsplit - 1;
       if (last) __hip_atomic_store(ticket + bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_s = last;
     }
@@ -1138,7 +1147,7 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(AttendParams p) {
       float M = -INFINITY;
 #pragma unroll
       for (int sp = 0; sp < DT_MAX_SPLIT; ++sp) {
-        if (sp < p.split) {
+        if (sp < nsplit) {
           const float* ps = part + ((size_t)sp * G + h) * (D + 2);
           ms[sp] = rd(ps + D + 1);
           ls[sp] = rd(ps + D);
@@ -1183,6 +1192,13 @@ int dt_split(int rows) {
 }
 
 int attend_rows(const sepcache* c, bool update) { return c->a + c->s + c->n + 1 + (update ? 1 : 0); }
+// Workgroups per (stream, KV head) of the tiled path, 0 if it does not apply:
+// the cache is too large, or a size does not fit the kernel's packed
+// arguments (B * Hkv, slots and Hq in 16 bits, Hkv in 8).
+int tiled_split(const sepcache* c, int Hq, bool update) {
+  if (c->B * c->Hkv >= 65536 || c->Hkv >= 256 || Hq >= 65536) return 0;
+  return dt_split(attend_rows(c, update));
+}
 // split path: workgroups per (stream, KV head)
 int attend_split(const sepcache* c, bool update) {
   const int per_split = SPLIT_THREADS / (c->d / 8) * SPLIT_MAXR;
@@ -1192,8 +1208,10 @@ int attend_split(const sepcache* c, bool update) {
 template <int D, int G, bool UPDATE, bool SHIFT>
 void launch_attend_t(const AttendParams& p, hipStream_t st) {
   if (p.tiled) {
+    const uint32_t dims0 = (uint32_t)(p.c.B * p.c.Hkv) | (uint32_t)p.c.Hkv << 16 | (uint32_t)p.split << 24;
+    const uint32_t dims1 = (uint32_t)p.c.slots | (uint32_t)p.Hq << 16;
     hipLaunchKernelGGL((decode_tiles<D, G, UPDATE, SHIFT>), dim3(p.c.B * p.c.Hkv * p.split), dim3(DT_THREADS), 0,
-                       st, p);
+                       st, p.c.state, p.c.k, p.c.v, p.q, p.is_sep, dims0, dims1, p.rev_log2_step, p);
   } else {
     hipLaunchKernelGGL((attend_part<D, G, UPDATE, SHIFT>), dim3(p.c.B * p.c.Hkv * p.split), dim3(SPLIT_THREADS), 0,
                        st, p);
@@ -1234,7 +1252,7 @@ AttendParams attend_params(const sepcache* c, int Hq, const void* q, float scale
   p.q = (const bf16*)q; p.o = (bf16*)o;
   p.k_new = p.v_new = nullptr; p.is_sep = nullptr;
   p.Hq = Hq; p.shift = shift;
-  const int sp = dt_split(attend_rows(c, update));
+  const int sp = tiled_split(c, Hq, update);
   p.tiled = sp > 0;
   p.split = p.tiled ? sp : attend_split(c, update);
   // both paths keep the tickets' area, so one workspace serves either
@@ -1265,8 +1283,7 @@ size_t sepcache_decode_ws_bytes(const sepcache* c, int Hq) {
   const size_t BH = (size_t)c->B * c->Hkv, G = Hq / c->Hkv;
   size_t need = 0;
   for (int update = 0; update < 2; ++update) {
-    const int rows = attend_rows(c, update);
-    const int sp = dt_split(rows);
+    const int sp = tiled_split(c, Hq, update);
     size_t b;
     if (sp == 1) b = 0;
     else if (sp > 1) b = dt_ticket_bytes((int)BH) + BH * sp * G * (c->d + 2) * 4;
