@@ -98,11 +98,16 @@ def test_cache_steps_against_simulator(case):
     assert int(cache.state[..., 6].abs().sum().cpu()) == 0  # no overflow flag
 
 
+# Consecutive fused steps with the window full, the state checked after each:
+# the evicted row walks over tiles held by different waves.
+RUN = list(range(600, 624))
+
+
 def test_llama_decode_full_run_sampled():
     wl = synth.LLAMA_DECODE
     say("cache", wl.name)
     flags, kb, vb = _setup(wl)
-    sample = [0, 1, 3, 4, 5, 100, 259, 260, 261, 600, 793, 1500, 2048, 4095, 6000, 8191]
+    sample = sorted({0, 1, 3, 4, 5, 100, 259, 260, 261, 793, 1500, 2048, 4095, 6000, 8191, *RUN})
     qb = _bf(wl.q_steps(sample))
     kd, vd = kb.cuda(), vb.cuda()
     fd = torch.from_numpy(flags).cuda()
@@ -119,7 +124,7 @@ def test_llama_decode_full_run_sampled():
             sims[b].append(int(flags[t, b]))
             sims[b].evict()
         if t in sample:
-            if t in (0, 5, 261, 793, 4095, 8191):
+            if t in (0, 5, 261, 793, 4095, 8191) or t in RUN:
                 torch.cuda.synchronize()
                 _check_state(cache, sims, kb, vb, t)
     torch.cuda.synchronize()
@@ -129,6 +134,46 @@ def test_llama_decode_full_run_sampled():
     ref, _ = orc.decode_run(qfull, as_f64(kb), as_f64(vb), flags, wl.a, wl.s, wl.n, wl.theta, True, sc,
                             out_steps=sample)
     for t in sample:
+        assert max_abs(as_f64(outs[t]), ref[t]) <= TOL_BF16, t
+
+
+def test_full_batch_steps_move_rows():
+    """The Llama decode geometry at its full batch (16 streams x 8 KV heads,
+    one workgroup each, 21 tiles of 16 rows) with many separators, so that
+    most window evictions move a row into the separator block (and, once
+    that block is full, drop its oldest).  Every fused step from the point
+    where the window is full is checked bit-exactly: the rows a step writes
+    (the appended token's slot, freed by the previous eviction, and the
+    moved row's destination) are ones it does not attend, while it reads the
+    moved row's old K/V wherever that row's tile lies."""
+    L = synth.LLAMA_DECODE
+    T0, T = 300, 396
+    wl = synth.DecodeWorkload("move-rows", 72, B=L.B, Hq=L.Hq, Hkv=L.Hkv, d=L.d, a=L.a, s=L.s, n=L.n, T=T, p=0.6)
+    say("cache-move-rows")
+    flags, kb, vb = _setup(wl)
+    steps = list(range(T0, T))
+    qb = _bf(wl.q_steps(steps)).cuda()
+    kd, vd, fd = kb.cuda(), vb.cuda(), torch.from_numpy(flags).cuda()
+    cache = sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta)
+    sims = [orc.SepCacheSim(wl.a, wl.s, wl.n) for _ in range(wl.B)]
+    sc = 1 / math.sqrt(wl.d)
+    outs = {}
+    for t in range(T):
+        if t >= T0:
+            outs[t] = cache.step(kd[t], vd[t], fd[t], qb[t - T0], sc, shift=True)
+        else:
+            cache.push(kd[t], vd[t], fd[t])
+        for b in range(wl.B):
+            sims[b].append(int(flags[t, b]))
+            sims[b].evict()
+        if t >= T0:
+            torch.cuda.synchronize()
+            _check_state(cache, sims, kb, vb, t)
+    qfull = np.zeros((T, wl.B, wl.Hq, wl.d))
+    qfull[steps] = as_f64(qb.cpu())
+    ref, _ = orc.decode_run(qfull, as_f64(kb), as_f64(vb), flags, wl.a, wl.s, wl.n, wl.theta, True, sc,
+                            out_steps=steps[::8])
+    for t in steps[::8]:
         assert max_abs(as_f64(outs[t]), ref[t]) <= TOL_BF16, t
 
 
