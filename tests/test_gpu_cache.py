@@ -55,8 +55,8 @@ SMALL = [
     (2, 16, 2, 128, 3, 5, 7, 45, 1.0, True, "push"),
     (2, 16, 2, 128, 3, 5, 7, 45, 1.0, True, "step"),
     (2, 4, 4, 64, 1, 8, 3, 45, 0.0, False, "push"),
-    (2, 8, 2, 64, 4, 200, 300, 700, 0.3, True, "step"),   # 505 slots: two workgroups per (stream, KV head)
-    (1, 4, 1, 128, 4, 400, 500, 1000, 0.4, True, "step"),  # 905 slots: three, merged through the workspace
+    (2, 8, 2, 64, 4, 200, 300, 700, 0.3, True, "step"),   # 505 slots: one workgroup of 32 tiles
+    (1, 4, 1, 128, 4, 400, 500, 1000, 0.4, True, "step"),  # 905 slots: two, merged through the workspace
     (1, 4, 2, 64, 2, 700, 400, 400, 0.5, False, "push"),   # 1103 slots: the split-and-merge kernels
     (1, 32, 8, 128, 4, 64, 256, 400, 0.12, True, "push"),
     (1, 32, 8, 128, 4, 64, 256, 400, 0.12, True, "step"),
