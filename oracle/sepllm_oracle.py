@@ -31,7 +31,14 @@ the design notes of the repository):
   * per decode step: append the token, evict from the window if it holds
     more than n entries (separator -> separator FIFO of capacity s, whose
     oldest entry is dropped on overflow; other tokens are dropped), attend;
-  * in-cache positions are ranks in the order sinks, separators, window.
+  * with a capacity c > a + s + n, the past-window block holds the
+    c - a - s - n = P tokens that left the local window most recently; the
+    window and the past window form one queue of at most n + P tokens, and
+    once it is full, the next token first makes its oldest P + 1 leave (the
+    separators among them join the separator FIFO in order, the others are
+    dropped), so the queue keeps n tokens with the new one;
+  * in-cache positions are ranks in the order sinks, separators, past
+    window, window.
 
 Everything is float64 (integers are exact).  Rows of the attention are
 computed in groups only to vectorise: every column left out of a group is one
@@ -269,22 +276,38 @@ def rope(x, pos, theta: float):
 
 class SepCacheSim:
     """Bookkeeping of one stream's SepCache: which original positions it holds
-    and in what order.  [PITH] key_machinery (initial, separator and window
-    blocks; leaving separators move to the separator cache, other leaving
-    tokens are dropped), [ANTH] streaming bullet (fixed-size cache).  The past
-    window block has size zero here (capacity a + s + n), so a token leaving
-    the window is classified at once; the separator block keeps its s most
-    recent separators (oldest dropped first)."""
+    and in what order.  [PITH] key_machinery (initial, separator, local-window
+    and past-window blocks under a capacity c; once the cache is full, the
+    past window's separators move to the separator cache and its other
+    tokens are dropped, a periodic evolution), [ANTH] streaming bullet
+    (fixed-size cache).  The separator block keeps its s most recent
+    separators (oldest dropped first).
 
-    def __init__(self, a: int, s: int, n: int):
+    c = None or a + s + n: no past window, so a token leaving the window is
+    classified at once (evict()).  c > a + s + n: the window and the past
+    window are one queue ``win`` of at most n + P tokens, P = c - a - s - n;
+    an append to a full queue first makes its oldest P + 1 tokens leave."""
+
+    def __init__(self, a: int, s: int, n: int, c: int | None = None):
         if n < 1 or a < 0 or s < 0:
             raise ValueError("need n >= 1, a >= 0, s >= 0")
+        if c is not None and c < a + s + n:
+            raise ValueError("need c >= a + s + n")
         self.a, self.s, self.n = a, s, n
+        self.P = 0 if c is None else c - a - s - n
         self.t = 0
         self.sinks: list[int] = []
         self.sep: deque[int] = deque()
         self.win: deque[int] = deque()
         self.flag: dict[int, int] = {}
+
+    def _leave(self, e: int) -> None:
+        """Token e leaves the window: a separator joins the separator FIFO,
+        anything else is dropped."""
+        if self.flag[e]:
+            self.sep.append(e)
+            if len(self.sep) > self.s:
+                self.sep.popleft()
 
     def append(self, flag: int) -> None:
         t = self.t
@@ -292,17 +315,16 @@ class SepCacheSim:
         if t < self.a:
             self.sinks.append(t)
         else:
+            if self.P > 0 and len(self.win) == self.n + self.P:
+                for _ in range(self.P + 1):
+                    self._leave(self.win.popleft())
             self.win.append(t)
         self.t += 1
 
     def evict(self) -> None:
-        if len(self.win) > self.n:
-            e = self.win.popleft()
-            if self.flag[e]:
-                self.sep.append(e)
-                if len(self.sep) > self.s:
-                    self.sep.popleft()
-            # a non-separator leaving the window is dropped
+        # without a past window: the oldest of n + 1 window tokens leaves
+        if len(self.win) > self.n + self.P:
+            self._leave(self.win.popleft())
 
     def order(self) -> list[int]:
         """Original positions held, in the cache's logical order."""
@@ -319,7 +341,7 @@ class SepCacheSim:
 
 
 def decode_run(q_all, k_all, v_all, flags, a: int, s: int, n: int, theta: float,
-               shift: bool, scale: float, out_steps=None, order_steps=()):
+               shift: bool, scale: float, out_steps=None, order_steps=(), c: int | None = None):
     """Streaming decode over a SepCache, one simulator per stream.
 
     q_all [T,B,Hq,d], k_all/v_all [T,B,Hkv,d] (keys pre-RoPE), flags [T,B].
@@ -331,7 +353,7 @@ def decode_run(q_all, k_all, v_all, flags, a: int, s: int, n: int, theta: float,
     T, B, Hq, d = q_all.shape
     Hkv = k_all.shape[2]
     g = Hq // Hkv
-    sims = [SepCacheSim(a, s, n) for _ in range(B)]
+    sims = [SepCacheSim(a, s, n, c) for _ in range(B)]
     want = set(range(T)) if out_steps is None else set(out_steps)
     want_order = set(order_steps)
     outs, orders = {}, {}

@@ -351,6 +351,65 @@ def test_cache_contents_closed_form_and_capacity():
             assert full_at is not None
 
 
+def _general_order(f, t, a, s, n, P):
+    """The cache after tokens 0..t, written out from the definition: the
+    window queue holds the last L tokens, where L counts the non-sink tokens
+    x appended so far up to n + P and then, each full queue emptying to n - 1
+    before the next token, cycles n, n + 1, ..., n + P; the separator block
+    holds the last s separators among the tokens that left the queue."""
+    x = t + 1 - a
+    if x <= 0:
+        return list(range(t + 1))
+    L = x if x <= n + P else n + (x - n - P - 1) % (P + 1)
+    left = [j for j in range(a, t + 1 - L) if f[j]]
+    return list(range(a)) + (left[-s:] if s else []) + list(range(t + 1 - L, t + 1))
+
+
+@pytest.mark.parametrize("a,s,n,c", [(4, 8, 6, 30), (2, 3, 5, 16), (0, 4, 3, 12), (3, 0, 4, 11), (1, 2, 1, 9),
+                                     (4, 64, 256, 800)])
+def test_general_cache_closed_form_and_usage_law(a, s, n, c):
+    """The four-block cache ([PITH] key_machinery): contents equal the
+    definition above at every step; the size never exceeds c; once the
+    separator block is full the size repeats with period P + 1 between
+    a + s + n and c, and its mean over a period is (n + c + a + s) / 2, the
+    average usage the page states (w = n)."""
+    P = c - a - s - n
+    steps = 3000 if c == 800 else 600
+    for p in (0.0, 0.12, 0.5, 1.0):
+        f = np.random.default_rng(int(p * 100) + c).random(steps) < p
+        sim = orc.SepCacheSim(a, s, n, c)
+        sizes, full = [], None
+        for t in range(steps):
+            sim.append(int(f[t]))
+            sim.evict()
+            got = sim.order()
+            assert got == _general_order(f, t, a, s, n, P), (p, t)
+            assert len(got) <= c
+            if full is None and len(sim.sep) == s and t + 1 - a > n + P:
+                full = t
+            sizes.append(len(got))
+        if p == 1.0:
+            assert full is not None
+            tail = sizes[full:]
+            k = (len(tail) // (P + 1)) * (P + 1)
+            for i in range(0, k, P + 1):
+                win = tail[i:i + P + 1]
+                assert min(win) == a + s + n and max(win) == c
+                assert sum(win) * 2 == (n + c + a + s) * (P + 1)
+
+
+def test_general_cache_reduces_to_the_bounded_window():
+    """c = a + s + n (no past window) is the cache without capacity."""
+    f = np.random.default_rng(3).random(400) < 0.3
+    for a, s, n in ((4, 8, 6), (0, 3, 1), (2, 0, 5)):
+        s1, s2 = orc.SepCacheSim(a, s, n), orc.SepCacheSim(a, s, n, a + s + n)
+        for t in range(len(f)):
+            for sim in (s1, s2):
+                sim.append(int(f[t]))
+                sim.evict()
+            assert s1.order() == s2.order(), (a, s, n, t)
+
+
 def test_decode_without_shift_equals_prefill_rows():
     T, B, Hq, Hkv, d = 48, 2, 4, 2, 8
     a, n, theta = 3, 6, 500000.0
