@@ -75,8 +75,8 @@ class PrefillLeg:
 
 
 class DecodeLeg:
-    def __init__(self, wl: synth.DecodeWorkload, layers: int, seed: int = 0):
-        self.wl, self.layers = wl, layers
+    def __init__(self, wl: synth.DecodeWorkload, layers: int, seed: int = 0, cap: int = 0):
+        self.wl, self.layers, self.cap = wl, layers, cap
         dev = "cuda"
         self.flags_np = wl.flags(seed)
         self.flags = torch.from_numpy(self.flags_np).to(dev)
@@ -85,7 +85,7 @@ class DecodeLeg:
         self.vp = torch.from_numpy(v).to(torch.bfloat16).to(dev)
         self.qp = torch.from_numpy(wl.q_steps(range(CHUNK), seed)).to(torch.bfloat16).to(dev)
         self.scale = 1.0 / math.sqrt(wl.d)
-        self.caches = [sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta) for _ in range(layers)]
+        self.caches = [sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta, cap=cap) for _ in range(layers)]
         self.out = torch.empty((layers, wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device=dev)
         self.fl_static = torch.zeros((CHUNK, wl.B), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
@@ -106,15 +106,22 @@ class DecodeLeg:
         """Bytes the path must move: every cached K and V row read once per
         token, plus q, o and the new K/V row (the separator move is an
         implementation choice and not counted).  Cache lengths follow from the
-        flags: sinks, separators that left the window (at most s), window."""
+        flags: sinks, separators that left the window queue (at most s), and
+        the queue, which holds the last L tokens: with P past-window entries
+        (capacity c = a + s + n + P) L counts up to n + P and then cycles
+        n, ..., n + P (a full queue empties to n - 1 before the next token)."""
         wl = self.wl
         T = wl.T
-        t = np.arange(T)[:, None]
+        P = max(0, self.cap - (wl.a + wl.s + wl.n))
+        t = np.arange(T)
         f = self.flags_np.astype(np.int64)
-        f_after_sinks = np.where(np.arange(T)[:, None] >= wl.a, f, 0)
+        f_after_sinks = np.where(t[:, None] >= wl.a, f, 0)
         csum = np.cumsum(f_after_sinks, axis=0)  # separators at positions <= t
-        left = np.where(t - wl.n >= 0, csum[np.clip(t - wl.n, 0, None)[:, 0]], 0)  # positions <= t-n
-        length = np.minimum(t + 1, wl.a) + np.minimum(left, wl.s) + np.minimum(np.maximum(t + 1 - wl.a, 0), wl.n)
+        x = np.maximum(t + 1 - wl.a, 0)  # tokens that entered the queue
+        L = np.where(x <= wl.n + P, x, wl.n + (x - wl.n - P - 1) % (P + 1))
+        last_left = t - L  # tokens at positions <= t - L have left the queue
+        left = np.where(last_left[:, None] >= 0, csum[np.clip(last_left, 0, None)], 0)
+        length = np.minimum(t + 1, wl.a)[:, None] + np.minimum(left, wl.s) + L[:, None]
         row = wl.Hkv * wl.d * 2
         per_layer = float(length.sum()) * row * 2 + T * wl.B * (2 * wl.Hq * wl.d * 2 + 2 * row)
         self.mean_len = float(length.mean())
@@ -206,6 +213,9 @@ def main():
     ap.add_argument("--profile-copy-mb", type=int, default=0,
                     help="also run one device-to-device copy of this many MiB (a known-size kernel that "
                          "calibrates HBM byte counters in a profiler run)")
+    ap.add_argument("--general-tokens", type=int, default=4096,
+                    help="tokens of the capacity-800 cache leg (the pages' streaming capacity; 0 skips it)")
+    ap.add_argument("--general-layers", type=int, default=8, help="layer caches of that leg")
     ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -244,6 +254,27 @@ def main():
         t_dec += dec.time_ms()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # The four-block cache at capacity c = 800 (a past window of 476 entries)
+    # on the same decode geometry: timed on its own, outside the step.
+    gen_out = None
+    if args.general_tokens > 0:
+        gen = DecodeLeg(synth.LLAMA_DECODE.with_(T=args.general_tokens), args.general_layers, args.seed, cap=800)
+        gen.step()
+        torch.cuda.synchronize()
+        t_gen = 0.0
+        for _ in range(args.steps):
+            gen.step()
+            torch.cuda.synchronize()
+            t_gen += gen.time_ms()
+        t_gen /= args.steps
+        gbs = gen.bytes / (t_gen * 1e-3) / 1e9
+        gen_out = {"config": {"B": gen.wl.B, "Hq": gen.wl.Hq, "Hkv": gen.wl.Hkv, "d": gen.wl.d, "a": gen.wl.a,
+                              "s": gen.wl.s, "n": gen.wl.n, "c": 800, "tokens": gen.wl.T,
+                              "layers": args.general_layers, "p": gen.wl.p, "shift": gen.wl.shift},
+                   "ms": round(t_gen, 3), "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                   "bytes": gen.bytes, "mean_cache_len": round(gen.mean_len, 2),
+                   "us_per_token_layer": round(t_gen * 1e3 / (gen.wl.T * args.general_layers), 3)}
+        del gen
     K = args.steps
     t_mask, t_fwd, t_bwd, t_dec = t_mask / K, t_fwd / K, t_bwd / K, t_dec / K
     pre_ms = t_mask + t_fwd + t_bwd
@@ -290,6 +321,8 @@ def main():
         "roofline": None,
         "rooflines": None,
     }
+    if gen_out is not None:
+        out["decode_c800"] = gen_out
     traffic = measured_traffic()
     dec_launch_us = t_dec * 1e3 / (dec.wl.T * args.layers)
     per_launch_bytes = dec.bytes / (dec.wl.T * args.layers)

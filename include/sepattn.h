@@ -154,20 +154,28 @@ SEPATTN_API int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mas
 /* ------------------------------------------------------------------------
  * SepCache: the streaming cache ([PITH] key_machinery; [ANTH] streaming
  * bullet) with a sink block of a entries, a separator block of s entries kept
- * first-in first-out, and a window of n entries (the newest token included).
- * Per step: append the new token, evict (a token leaving the window moves to
- * the separator block if it is a separator, dropping that block's oldest
- * entry when full, and is dropped otherwise), then decode.  After eviction
- * the cache holds at most a + s + n entries.  The cache's logical order is
- * sinks, separators (oldest first), window (oldest first), which is
- * ascending original position.
+ * first-in first-out, a window of n entries (the newest token included) and,
+ * with a capacity c > a + s + n, a past window of P = c - a - s - n entries.
+ * A token leaving the window (or, with a past window, the past window) moves
+ * to the separator block if it is a separator, dropping that block's oldest
+ * entry when full, and is dropped otherwise.
+ *   c = 0 or a + s + n (no past window).  Per step: append the new token,
+ *   evict (the oldest of n + 1 window entries leaves), then decode: the
+ *   cache holds at most a + s + n entries.
+ *   c > a + s + n.  The window and past window form one queue of at most
+ *   n + P tokens.  An append to a full queue first makes its oldest P + 1
+ *   leave (a flush), so the queue then holds n; evict does nothing.  The
+ *   cache holds at most c entries, and once the separator block is full its
+ *   size cycles a + s + n, ..., c, with mean (n + c + a + s) / 2.
+ * The cache's logical order is sinks, separators (oldest first), past
+ * window, window (oldest first), which is ascending original position.
  *
  * All streams of a batch share the step: stream b appends its own token and
  * flag.  Physical slots per stream and KV head: [0, a) sinks, [a, a+s)
- * separator ring, [a+s, a+s+n+1) window ring (one spare slot for the
- * appended token).  Every KV head keeps its own copy of the slot metadata and
- * counters (all copies hold the same values), so the work of one (stream, KV
- * head) never waits on another workgroup.
+ * separator ring, [a+s, slots) window ring of n + P + 1 slots (one spare for
+ * the appended token), slots = a + s + n + P + 1.  Every KV head keeps its own
+ * copy of the slot metadata and counters (all copies hold the same values),
+ * so the work of one (stream, KV head) never waits on another workgroup.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int B, Hkv, d;       /* streams, KV heads, head dim (64 or 128)              */
@@ -182,20 +190,25 @@ typedef struct {
                           separator flag of the window's oldest entry          */
   float theta;         /* RoPE base: pair (i, i + d/2) turns by p * theta^(-2i/d)
                           at position p                                        */
+  int c;               /* capacity: 0 or a + s + n (no past window), or more
+                          (a past window of c - a - s - n entries)             */
 } sepcache;
 
-/* Physical slots per stream and KV head: a + s + n + 1. */
-SEPATTN_API int sepcache_slots(int a, int s, int n);
+/* Physical slots per stream and KV head: max(c, a + s + n) + 1; -1 for
+ * invalid sizes (a < 0, s < 0, n < 1, or 0 < c < a + s + n). */
+SEPATTN_API int sepcache_slots(int a, int s, int n, int c);
 /* Empty every stream (slot_pos = -1, counters 0, K and V zero) of every KV
  * head. */
 SEPATTN_API int sepcache_reset(const sepcache* c, void* stream);
 /* Append token t of every stream: k_new, v_new bf16 [B, Hkv, d] contiguous,
  * is_sep device uint8 [B].  Token t < a becomes a sink, later tokens enter the
- * window.  Call sepcache_evict before the next append. */
+ * window (with a past window, after the flush of a full queue: two kernels).
+ * Call sepcache_evict before the next append. */
 SEPATTN_API int sepcache_append(const sepcache* c, const void* k_new, const void* v_new,
                     const uint8_t* is_sep, void* stream);
 /* If a stream's window holds more than n entries, its oldest entry leaves:
- * to the separator block (separator) or dropped (other). */
+ * to the separator block (separator) or dropped (other).  With a past window
+ * the append has made room already and this does nothing. */
 SEPATTN_API int sepcache_evict(const sepcache* c, void* stream);
 /* append + evict in one launch. */
 SEPATTN_API int sepcache_push(const sepcache* c, const void* k_new, const void* v_new,
@@ -210,8 +223,8 @@ SEPATTN_API int sepcache_push(const sepcache* c, const void* k_new, const void* 
  * RoPE angles are computed on the device: position times frequency is
  * reduced modulo one turn in double precision for original positions and in
  * fp32 for ranks.  The cache is only read.
- * Caches with at most 1024 rows (a + s + n + 1, plus the appended token's row
- * for sepcache_step) run as one kernel: the rows are shared by
+ * Caches with at most 1024 rows (slots, plus the appended token's row for
+ * sepcache_step) run as one kernel: the rows are shared by
  * ceil(rows / 512) workgroups per (stream, KV head), and with more than one
  * the last to finish merges the others' partial results from the workspace.
  * There the rotated keys and query enter the score product as bf16 and the
@@ -230,11 +243,12 @@ SEPATTN_API int sepcache_decode(const sepcache* c, int Hq, const void* q, float 
 /* One decode step: append the new token (k_new, v_new, is_sep as for
  * sepcache_append), evict, and attend (q, o, workspace as for
  * sepcache_decode); the same result as sepcache_push then sepcache_decode,
- * in two launches that read the cache once. */
+ * reading the cache once (with a past window, the flush of a full queue runs
+ * as a kernel of its own first). */
 SEPATTN_API int sepcache_step(const sepcache* c, const void* k_new, const void* v_new,
                   const uint8_t* is_sep, int Hq, const void* q, float scale, int shift,
                   void* o, void* workspace, size_t workspace_bytes, void* stream);
-/* Original positions in logical order: pos [B, a+s+n] (unused tail -1),
+/* Original positions in logical order: pos [B, slots - 1] (unused tail -1),
  * len [B] entries held.  For bit-exact checks against a reference. */
 SEPATTN_API int sepcache_export_order(const sepcache* c, int32_t* pos, int32_t* len, void* stream);
 

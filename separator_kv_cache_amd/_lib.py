@@ -29,7 +29,7 @@ class SepattnShape(ctypes.Structure):
 class SepCacheStruct(ctypes.Structure):
     _fields_ = [("B", c_int), ("Hkv", c_int), ("d", c_int), ("a", c_int), ("s", c_int), ("n", c_int),
                 ("k", c_void_p), ("v", c_void_p), ("slot_pos", c_void_p), ("slot_sep", c_void_p),
-                ("state", c_void_p), ("theta", c_float)]
+                ("state", c_void_p), ("theta", c_float), ("c", c_int)]
 
 
 _SIGS = {
@@ -45,7 +45,7 @@ _SIGS = {
     "sepattn_bwd": (c_int, [POINTER(SepattnShape), c_int, POINTER(SepattnMask), c_void_p, c_void_p,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                             c_void_p, c_void_p, c_size_t, c_void_p]),
-    "sepcache_slots": (c_int, [c_int, c_int, c_int]),
+    "sepcache_slots": (c_int, [c_int, c_int, c_int, c_int]),
     "sepcache_reset": (c_int, [POINTER(SepCacheStruct), c_void_p]),
     "sepcache_append": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, c_void_p, c_void_p]),
     "sepcache_evict": (c_int, [POINTER(SepCacheStruct), c_void_p]),

@@ -132,15 +132,17 @@ def sepattn_bwd(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, work
 
 
 class SepCache:
-    """A SepCache for B streams (bf16 K/V)."""
+    """A SepCache for B streams (bf16 K/V); cap is the capacity c (0 or
+    a + s + n: no past window)."""
 
     def __init__(self, B: int, Hkv: int, d: int, a: int, s: int, n: int, theta: float = 500000.0,
-                 device="cuda"):
+                 cap: int = 0, device="cuda"):
         lib = _lib.load()
-        slots = lib.sepcache_slots(a, s, n)
+        slots = lib.sepcache_slots(a, s, n, cap)
         if slots < 0:
-            raise ValueError(f"bad cache sizes a={a} s={s} n={n}")
+            raise ValueError(f"bad cache sizes a={a} s={s} n={n} c={cap}")
         self.B, self.Hkv, self.d, self.a, self.s, self.n, self.slots = B, Hkv, d, a, s, n, slots
+        self.cap = slots - 1
         self.k = torch.zeros((B, Hkv, slots, d), dtype=torch.bfloat16, device=device)
         self.v = torch.zeros((B, Hkv, slots, d), dtype=torch.bfloat16, device=device)
         self.slot_pos = torch.empty((B, Hkv, slots), dtype=torch.int32, device=device)
@@ -152,6 +154,7 @@ class SepCache:
         c.slot_pos, c.slot_sep, c.state = (self.slot_pos.data_ptr(), self.slot_sep.data_ptr(),
                                            self.state.data_ptr())
         c.theta = float(theta)
+        c.c = int(cap)
         self.c = c
         self._ws = None
         self.reset()
@@ -210,8 +213,8 @@ class SepCache:
         return torch.empty_like(q) if out is None else out
 
     def export_order(self):
-        """sepcache_export_order: (pos int32 [B, a+s+n], len int32 [B])."""
-        pos = torch.empty((self.B, self.a + self.s + self.n), dtype=torch.int32, device=self.k.device)
+        """sepcache_export_order: (pos int32 [B, slots - 1], len int32 [B])."""
+        pos = torch.empty((self.B, self.cap), dtype=torch.int32, device=self.k.device)
         ln = torch.empty((self.B,), dtype=torch.int32, device=self.k.device)
         check(_lib.load().sepcache_export_order(ctypes.byref(self.c), _ptr(pos), _ptr(ln), _stream()))
         return pos, ln

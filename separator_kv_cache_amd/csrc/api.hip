@@ -197,9 +197,10 @@ int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const 
 
 // ------------------------------------------------------------------ SepCache
 
-int sepcache_slots(int a, int s, int n) {
-  if (a < 0 || s < 0 || n < 1) return -1;
-  return a + s + n + 1;
+int sepcache_slots(int a, int s, int n, int c) {
+  if (a < 0 || s < 0 || n < 1 || c < 0 || (c > 0 && (int64_t)c < (int64_t)a + s + n)) return -1;
+  const int64_t cap = c > 0 ? (int64_t)c : (int64_t)a + s + n;
+  return cap + 1 > 65536 ? -1 : (int)(cap + 1);
 }
 
 static int check_cache(const sepcache* c, const char* who) {
@@ -208,7 +209,9 @@ static int check_cache(const sepcache* c, const char* who) {
   if (c->d != 64 && c->d != 128) return sepattn_fail(SEPATTN_ENOTSUP, "%s: head dim %d (64 or 128)", who, c->d);
   if (c->a < 0 || c->s < 0 || c->n < 1)
     return sepattn_fail(SEPATTN_EINVAL, "%s: need a >= 0, s >= 0, n >= 1 (a=%d s=%d n=%d)", who, c->a, c->s, c->n);
-  if ((int64_t)c->a + c->s + c->n + 1 > 65536) return sepattn_fail(SEPATTN_EINVAL, "%s: cache too large", who);
+  if (c->c < 0 || (c->c > 0 && (int64_t)c->c < (int64_t)c->a + c->s + c->n))
+    return sepattn_fail(SEPATTN_EINVAL, "%s: capacity c=%d below a + s + n = %d", who, c->c, c->a + c->s + c->n);
+  if (sepcache_slots(c->a, c->s, c->n, c->c) < 0) return sepattn_fail(SEPATTN_EINVAL, "%s: cache too large", who);
   if (!c->k || !c->v || !c->slot_pos || !c->slot_sep || !c->state)
     return sepattn_fail(SEPATTN_EINVAL, "%s: null cache array", who);
   if (!aligned16(c->k) || !aligned16(c->v)) return sepattn_fail(SEPATTN_EINVAL, "%s: K/V not 16-byte aligned", who);
@@ -244,7 +247,7 @@ int sepcache_push(const sepcache* c, const void* k_new, const void* v_new, const
 
 size_t sepcache_decode_workspace_size(const sepcache* c, int Hq) {
   if (!c || c->B <= 0 || c->Hkv <= 0 || Hq <= 0 || Hq % c->Hkv != 0 || (c->d != 64 && c->d != 128) ||
-      c->a < 0 || c->s < 0 || c->n < 1)
+      sepcache_slots(c->a, c->s, c->n, c->c) < 0)
     return 0;
   return sepcache_decode_ws_bytes(c, Hq);
 }

@@ -24,21 +24,27 @@ namespace {
 enum { ST_T = 0, ST_NSINK, ST_SEPH, ST_SEPC, ST_WINH, ST_WINC, ST_FLAGS, ST_OLDSEP };
 constexpr int FLAG_WINDOW_OVERFLOW = 1;
 
+// n is the window queue's capacity: the window plus the past window (P
+// entries, 0 without one).  The step logic below (append, evict, ranks) only
+// needs that capacity; the flush of a full queue alone needs P.
 struct CacheParams {
   bf16* k;
   bf16* v;
   int32_t* slot_pos;
   uint8_t* slot_sep;
   int32_t* state;
-  int B, Hkv, d, a, s, n, slots;
+  int B, Hkv, d, a, s, n, slots, P;
 };
+
+int past_entries(const sepcache* c) { return c->c > c->a + c->s + c->n ? c->c - (c->a + c->s + c->n) : 0; }
 
 CacheParams make_params(const sepcache* c) {
   CacheParams p;
   p.k = (bf16*)c->k; p.v = (bf16*)c->v;
   p.slot_pos = c->slot_pos; p.slot_sep = c->slot_sep; p.state = c->state;
-  p.B = c->B; p.Hkv = c->Hkv; p.d = c->d; p.a = c->a; p.s = c->s; p.n = c->n;
-  p.slots = c->a + c->s + c->n + 1;
+  p.P = past_entries(c);
+  p.B = c->B; p.Hkv = c->Hkv; p.d = c->d; p.a = c->a; p.s = c->s; p.n = c->n + p.P;
+  p.slots = c->a + c->s + p.n + 1;
   return p;
 }
 
@@ -201,6 +207,68 @@ __global__ __launch_bounds__(64) void update_kernel(CacheParams p, const bf16* k
              vb + (size_t)tr.ev_dst * p.d);
   __syncthreads();
   if (threadIdx.x == 0) commit(tr, st, spos, ssep, new_sep, ev_pos, new_oldsep);
+}
+
+// With a past window (P >= 1): before a token is appended to a full window
+// queue (n + P entries), its oldest P + 1 entries leave it in order.  The
+// separators among them join the separator ring, which keeps its s most
+// recent; the others are dropped; the queue keeps its newest n - 1.  One wave
+// per (stream, KV head); nothing happens unless the queue is full.
+__global__ __launch_bounds__(64) void flush_kernel(CacheParams p) {
+  const int bh = blockIdx.x, lane = threadIdx.x;
+  int32_t* st = p.state + (size_t)bh * 8;
+  int32_t* spos = p.slot_pos + (size_t)bh * p.slots;
+  uint8_t* ssep = p.slot_sep + (size_t)bh * p.slots;
+  bf16* kb = p.k + (size_t)bh * p.slots * p.d;
+  bf16* vb = p.v + (size_t)bh * p.slots * p.d;
+  const Counters c = load_counters(st);
+  if (c.winc < p.n) return;  // p.n = n + P, the queue's capacity
+  const int W = p.n + 1, m = p.P + 1, q0 = p.a + p.s;
+  auto qslot = [&](int e) { return q0 + (c.winh + e) % W; };
+  // the number of separators among the leaving entries
+  int M = 0;
+  for (int e0 = 0; e0 < m; e0 += 64) {
+    const bool sep = e0 + lane < m && ssep[qslot(e0 + lane)] != 0;
+    M += __popcll(__ballot(sep));
+  }
+  // separator i (in order) goes to ring slot (seph + sepc + i) mod s; of
+  // more than s, only the last s survive, so only those are written and
+  // every ring slot is written once
+  const int keep_from = max(0, M - p.s);
+  int before = 0;
+  for (int e0 = 0; e0 < m; e0 += 64) {
+    const int e = e0 + lane;
+    const int src = qslot(e < m ? e : 0);
+    const bool sep = e < m && ssep[src] != 0;
+    const uint64_t bal = __ballot(sep);
+    const int i = before + __popcll(bal & ((1ull << lane) - 1ull));
+    if (sep && p.s > 0 && i >= keep_from) {
+      const int dst = p.a + (c.seph + c.sepc + i) % p.s;
+      for (int ch = 0; ch < p.d / 8; ++ch) {
+        st16(kb + (size_t)dst * p.d + ch * 8, ld16(kb + (size_t)src * p.d + ch * 8));
+        st16(vb + (size_t)dst * p.d + ch * 8, ld16(vb + (size_t)src * p.d + ch * 8));
+      }
+      spos[dst] = spos[src];
+      ssep[dst] = 1;
+    }
+    before += __popcll(bal);
+  }
+  // the leaving entries' slots now hold none (this wave read them above)
+  for (int e = lane; e < m; e += 64) {
+    spos[qslot(e)] = -1;
+    ssep[qslot(e)] = 0;
+  }
+  if (lane == 0) {
+    Counters c1 = c;
+    if (p.s > 0) {
+      c1.seph = (c.seph + max(0, c.sepc + M - p.s)) % p.s;
+      c1.sepc = min(p.s, c.sepc + M);
+    }
+    c1.winh = (c.winh + m) % W;
+    c1.winc = c.winc - m;
+    c1.oldsep = c1.winc > 0 ? ssep[q0 + c1.winh] : 0;  // a slot that stays
+    store_counters(st, c1);
+  }
 }
 
 __global__ void export_kernel(CacheParams p, int32_t* pos, int32_t* len) {
@@ -1191,7 +1259,7 @@ int dt_split(int rows) {
   return sp <= DT_MAX_SPLIT ? sp : 0;
 }
 
-int attend_rows(const sepcache* c, bool update) { return c->a + c->s + c->n + 1 + (update ? 1 : 0); }
+int attend_rows(const sepcache* c, bool update) { return make_params(c).slots + (update ? 1 : 0); }
 // Workgroups per (stream, KV head) of the tiled path, 0 if it does not apply:
 // the cache is too large, or a size does not fit the kernel's packed
 // arguments (B * Hkv, slots and Hq in 16 bits, Hkv in 8).
@@ -1272,8 +1340,16 @@ int sepcache_launch_reset(const sepcache* c, hipStream_t st) {
   return sepattn_hip_check(hipGetLastError(), "reset launch");
 }
 
+// With a past window, an append first flushes a full window queue.
+static int launch_flush(const sepcache* c, hipStream_t st) {
+  if (past_entries(c) == 0) return SEPATTN_OK;
+  hipLaunchKernelGGL(flush_kernel, dim3(c->B * c->Hkv), dim3(64), 0, st, make_params(c));
+  return sepattn_hip_check(hipGetLastError(), "flush launch");
+}
+
 int sepcache_launch_update(const sepcache* c, const void* k_new, const void* v_new, const uint8_t* is_sep,
                            int do_append, int do_evict, hipStream_t st) {
+  if (do_append) SEPATTN_TRY(launch_flush(c, st));
   hipLaunchKernelGGL(update_kernel, dim3(c->B * c->Hkv), dim3(64), 0, st, make_params(c), (const bf16*)k_new,
                      (const bf16*)v_new, is_sep, do_append, do_evict);
   return sepattn_hip_check(hipGetLastError(), "update launch");
@@ -1301,6 +1377,7 @@ int sepcache_launch_decode(const sepcache* c, int Hq, const void* q, float scale
 
 int sepcache_launch_step(const sepcache* c, const void* k_new, const void* v_new, const uint8_t* is_sep, int Hq,
                          const void* q, float scale, int shift, void* o, void* ws, hipStream_t st) {
+  SEPATTN_TRY(launch_flush(c, st));
   AttendParams p = attend_params(c, Hq, q, scale, shift, o, ws, true);
   p.k_new = (const bf16*)k_new; p.v_new = (const bf16*)v_new; p.is_sep = is_sep;
   return dispatch_attend(p, Hq / c->Hkv, true, st);

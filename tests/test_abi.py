@@ -89,8 +89,11 @@ def test_argument_validation_without_gpu():
     assert need >= 1 * 4 * 64 * 4
     assert lib.sepattn_bwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, p, p, p, 0.1, p, p, p, p,
                            need - 1, None) == _lib.ESPACE
-    assert lib.sepcache_slots(4, 64, 256) == 325
-    assert lib.sepcache_slots(4, 64, 0) == -1
+    assert lib.sepcache_slots(4, 64, 256, 0) == 325
+    assert lib.sepcache_slots(4, 64, 256, 324) == 325
+    assert lib.sepcache_slots(4, 64, 256, 800) == 801  # a past window of 476 entries
+    assert lib.sepcache_slots(4, 64, 256, 300) == -1   # capacity below a + s + n
+    assert lib.sepcache_slots(4, 64, 0, 0) == -1
     c = _lib.SepCacheStruct()
     c.B, c.Hkv, c.d, c.a, c.s, c.n = 2, 2, 64, 4, 8, 0
     assert lib.sepcache_reset(ctypes.byref(c), None) == _lib.EINVAL
@@ -109,4 +112,8 @@ def test_argument_validation_without_gpu():
     assert need > 0
     assert lib.sepcache_decode(ctypes.byref(c), 4, p, 0.1, 1, p, p, need - 1, None) == _lib.ESPACE
     c.s = 8
+    c.c = 20  # below a + s + n = 28
+    assert lib.sepcache_reset(ctypes.byref(c), None) == _lib.EINVAL
+    assert b"capacity" in lib.sepattn_last_error()
+    c.c = 0
     assert lib.sepcache_step(ctypes.byref(c), None, p, p, 4, p, 0.1, 1, p, None, 0, None) == _lib.EINVAL

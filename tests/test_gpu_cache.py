@@ -60,18 +60,28 @@ SMALL = [
     (1, 4, 2, 64, 2, 700, 400, 400, 0.5, False, "push"),   # 1103 slots: the split-and-merge kernels
     (1, 32, 8, 128, 4, 64, 256, 400, 0.12, True, "push"),
     (1, 32, 8, 128, 4, 64, 256, 400, 0.12, True, "step"),
+    # with a capacity c > a + s + n (a past window of c - a - s - n entries);
+    # the last field is c
+    (3, 4, 2, 64, 2, 3, 5, 90, 0.4, True, "step", 16),
+    (3, 4, 2, 128, 2, 3, 5, 90, 0.4, False, "push", 16),
+    (2, 4, 2, 64, 2, 3, 5, 90, 0.5, True, "split", 14),
+    (2, 8, 2, 128, 3, 0, 4, 70, 0.5, True, "step", 12),    # s = 0: the flush drops everything
+    (2, 8, 1, 128, 1, 2, 1, 60, 0.6, False, "step", 9),    # n = 1
+    (2, 8, 2, 128, 4, 64, 256, 1300, 0.12, True, "step", 800),  # c = 800: 801 slots, two workgroups
+    (1, 4, 2, 64, 2, 300, 400, 900, 0.5, False, "push", 1100),  # 1101 slots: the split-and-merge kernels
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=[f"cache{i}" for i in range(len(SMALL))])
 def test_cache_steps_against_simulator(case):
-    B, Hq, Hkv, d, a, s, n, T, p, shift, api = case
+    B, Hq, Hkv, d, a, s, n, T, p, shift, api = case[:11]
+    cap = case[11] if len(case) > 11 else None
     say("cache", case)
     wl = synth.DecodeWorkload("small", 70, B=B, Hq=Hq, Hkv=Hkv, d=d, a=a, s=s, n=n, T=T, p=p, shift=shift)
     flags, kb, vb = _setup(wl)
     qb = _bf(wl.q_steps(range(T)))
-    cache = sa.SepCache(B, Hkv, d, a, s, n, wl.theta)
-    sims = [orc.SepCacheSim(a, s, n) for _ in range(B)]
+    cache = sa.SepCache(B, Hkv, d, a, s, n, wl.theta, cap=cap or 0)
+    sims = [orc.SepCacheSim(a, s, n, cap) for _ in range(B)]
     sc = 1 / math.sqrt(d)
     outs = []
     for t in range(T):
@@ -88,11 +98,11 @@ def test_cache_steps_against_simulator(case):
         for b in range(B):
             sims[b].append(int(flags[t, b]))
             sims[b].evict()
-        if t < 12 or t % 7 == 0 or t == T - 1:
+        if t < 12 or t % 7 == 0 or t == T - 1 or cache.slots <= 64:
             torch.cuda.synchronize()
             _check_state(cache, sims, kb, vb, t)
     torch.cuda.synchronize()
-    ref, _ = orc.decode_run(as_f64(qb), as_f64(kb), as_f64(vb), flags, a, s, n, wl.theta, shift, sc)
+    ref, _ = orc.decode_run(as_f64(qb), as_f64(kb), as_f64(vb), flags, a, s, n, wl.theta, shift, sc, c=cap)
     for t in range(T):
         assert max_abs(as_f64(outs[t]), ref[t]) <= TOL_BF16, t
     assert int(cache.state[..., 6].abs().sum().cpu()) == 0  # no overflow flag
