@@ -201,6 +201,35 @@ def measured_traffic() -> dict:
     return out if sha == kernel_sources_sha256() else {}
 
 
+def handoff_leg(wl: synth.DecodeWorkload, L: int, seed: int, reps: int = 50) -> dict:
+    """sepcache_prefill of an L-token prompt into one layer's caches.  Its
+    algorithmic bytes: the K/V rows of the entries kept (read once) and every
+    slot's K/V and metadata and the counters (written once); the few mask
+    words it reads per (stream, KV head) are left out."""
+    dev = "cuda"
+    tok = torch.from_numpy(synth.tokens_iid(seed, 90, wl.B, L, wl.p)).to(dev)
+    m = sa.build_mask(tok, synth.SEP_IDS, wl.a, wl.n)
+    gen = torch.Generator(device=dev).manual_seed(seed)
+    k = torch.randn((wl.B, wl.Hkv, L, wl.d), generator=gen, device=dev).to(torch.bfloat16)
+    v = torch.randn((wl.B, wl.Hkv, L, wl.d), generator=gen, device=dev).to(torch.bfloat16)
+    cache = sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta)
+    cache.prefill(k, v, m)
+    torch.cuda.synchronize()
+    entries = int((cache.slot_pos[:, 0] >= 0).sum())  # over streams, one KV head
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        cache.prefill(k, v, m)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    row = wl.d * 2
+    nbytes = entries * wl.Hkv * row * 2 + wl.B * wl.Hkv * (cache.slots * (row * 2 + 5) + 32)
+    return {"config": {"B": wl.B, "Hkv": wl.Hkv, "d": wl.d, "a": wl.a, "s": wl.s, "n": wl.n, "prompt": L},
+            "us": round(us, 3), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "entries": entries}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +245,8 @@ def main():
     ap.add_argument("--general-tokens", type=int, default=4096,
                     help="tokens of the capacity-800 cache leg (the pages' streaming capacity; 0 skips it)")
     ap.add_argument("--general-layers", type=int, default=8, help="layer caches of that leg")
+    ap.add_argument("--handoff-tokens", type=int, default=4096,
+                    help="prompt length of the prefill-to-cache hand-off leg (0 skips it)")
     ap.add_argument("--seed", type=int, default=0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -275,6 +306,11 @@ def main():
                    "bytes": gen.bytes, "mean_cache_len": round(gen.mean_len, 2),
                    "us_per_token_layer": round(t_gen * 1e3 / (gen.wl.T * args.general_layers), 3)}
         del gen
+    # Prompt hand-off: seed the Llama decode caches (16 streams x 8 KV heads,
+    # 324 entries) from a prompt's K/V and mask metadata, timed on its own.
+    hand_out = None
+    if args.handoff_tokens > 0:
+        hand_out = handoff_leg(synth.LLAMA_DECODE, args.handoff_tokens, args.seed)
     K = args.steps
     t_mask, t_fwd, t_bwd, t_dec = t_mask / K, t_fwd / K, t_bwd / K, t_dec / K
     pre_ms = t_mask + t_fwd + t_bwd
@@ -323,6 +359,8 @@ def main():
     }
     if gen_out is not None:
         out["decode_c800"] = gen_out
+    if hand_out is not None:
+        out["prefill_handoff"] = hand_out
     traffic = measured_traffic()
     dec_launch_us = t_dec * 1e3 / (dec.wl.T * args.layers)
     per_launch_bytes = dec.bytes / (dec.wl.T * args.layers)

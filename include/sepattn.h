@@ -248,6 +248,22 @@ SEPATTN_API int sepcache_decode(const sepcache* c, int Hq, const void* q, float 
 SEPATTN_API int sepcache_step(const sepcache* c, const void* k_new, const void* v_new,
                   const uint8_t* is_sep, int Hq, const void* q, float scale, int shift,
                   void* o, void* workspace, size_t workspace_bytes, void* stream);
+/* Prompt hand-off from prefill: seeds every stream's cache with a prompt of
+ * m->L tokens, leaving the state that sepcache_reset followed by m->L calls
+ * of sepcache_push would leave (the sinks, the separators that left the
+ * window, the window; with a past window, its queue), bit for bit.
+ *   k, v      bf16 [B, Hkv, L, d], keys before RoPE, addressed with element
+ *             strides k_stride / v_stride (host int64 [3]: batch, head,
+ *             token; multiples of 8) and a contiguous last dimension;
+ *   m         the prompt's mask metadata from sepattn_build_mask, with
+ *             m->B == c->B and m->a == c->a (its is_sep, sep_idx and
+ *             sep_before name the separators the cache keeps; m->n plays no
+ *             part).
+ * Every slot is written, and the counters: an empty window-ring slot gets
+ * the K/V of the token that last left it, as pushing leaves it, and other
+ * empty slots zeros, as after a reset.  One launch. */
+SEPATTN_API int sepcache_prefill(const sepcache* c, const void* k, const void* v, const int64_t* k_stride,
+                     const int64_t* v_stride, const sepattn_mask* m, void* stream);
 /* Original positions in logical order: pos [B, slots - 1] (unused tail -1),
  * len [B] entries held.  For bit-exact checks against a reference. */
 SEPATTN_API int sepcache_export_order(const sepcache* c, int32_t* pos, int32_t* len, void* stream);

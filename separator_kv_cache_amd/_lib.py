@@ -54,6 +54,8 @@ _SIGS = {
     "sepcache_decode": (c_int, [POINTER(SepCacheStruct), c_int, c_void_p, c_float, c_int, c_void_p,
                                 c_void_p, c_size_t, c_void_p]),
     "sepcache_export_order": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, c_void_p]),
+    "sepcache_prefill": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, POINTER(c_int64), POINTER(c_int64),
+                                 POINTER(SepattnMask), c_void_p]),
     "sepcache_step": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_float,
                               c_int, c_void_p, c_void_p, c_size_t, c_void_p]),
 }

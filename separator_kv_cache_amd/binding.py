@@ -212,6 +212,18 @@ class SepCache:
             raise ValueError("q must be contiguous bf16 [B, Hq, d]")
         return torch.empty_like(q) if out is None else out
 
+    def prefill(self, k, v, m: Mask):
+        """sepcache_prefill: seed every stream with a prompt of m.L tokens
+        (k, v bf16 [B, Hkv, L, d], keys before RoPE; m its mask metadata)."""
+        for t in (k, v):
+            if (t.dtype != torch.bfloat16 or t.dim() != 4 or t.shape[0] != self.B or t.shape[1] != self.Hkv
+                    or t.shape[2] != m.L or t.shape[3] != self.d or t.stride(-1) != 1):
+                raise ValueError("k/v must be bf16 [B, Hkv, L, d] with a contiguous last dimension")
+        ks = (ctypes.c_int64 * 3)(*k.stride()[:3])
+        vs = (ctypes.c_int64 * 3)(*v.stride()[:3])
+        check(_lib.load().sepcache_prefill(ctypes.byref(self.c), _ptr(k), _ptr(v), ks, vs, ctypes.byref(m.c),
+                                           _stream()))
+
     def export_order(self):
         """sepcache_export_order: (pos int32 [B, slots - 1], len int32 [B])."""
         pos = torch.empty((self.B, self.cap), dtype=torch.int32, device=self.k.device)

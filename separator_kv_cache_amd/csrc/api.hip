@@ -27,6 +27,8 @@ size_t sepcache_decode_ws_bytes(const sepcache* c, int Hq);
 int sepcache_launch_decode(const sepcache* c, int Hq, const void* q, float scale, int shift, void* o,
                            void* ws, hipStream_t st);
 int sepcache_launch_export(const sepcache* c, int32_t* pos, int32_t* len, hipStream_t st);
+int sepcache_launch_prefill(const sepcache* c, const void* k, const void* v, const int64_t* ks, const int64_t* vs,
+                            const sepattn_mask* m, hipStream_t st);
 int sepcache_launch_step(const sepcache* c, const void* k_new, const void* v_new, const uint8_t* is_sep, int Hq,
                          const void* q, float scale, int shift, void* o, void* ws, hipStream_t st);
 
@@ -292,6 +294,22 @@ int sepcache_step(const sepcache* c, const void* k_new, const void* v_new, const
   SEPATTN_TRY(check_ws(c, Hq, workspace, workspace_bytes, "step"));
   SEPATTN_TRY(sepattn_check_device());
   return sepcache_launch_step(c, k_new, v_new, is_sep, Hq, q, scale, shift, o, workspace, (hipStream_t)stream);
+}
+
+int sepcache_prefill(const sepcache* c, const void* k, const void* v, const int64_t* k_stride,
+                     const int64_t* v_stride, const sepattn_mask* m, void* stream) {
+  g_err[0] = 0;
+  SEPATTN_TRY(check_cache(c, "prefill"));
+  SEPATTN_TRY(check_mask(m, "prefill"));
+  if (m->B != c->B) return sepattn_fail(SEPATTN_EINVAL, "prefill: mask B=%d, cache B=%d", m->B, c->B);
+  if (m->a != c->a) return sepattn_fail(SEPATTN_EINVAL, "prefill: mask a=%d, cache a=%d", m->a, c->a);
+  if (!k || !v || !k_stride || !v_stride) return sepattn_fail(SEPATTN_EINVAL, "prefill: null K/V or strides");
+  if (!aligned16(k) || !aligned16(v)) return sepattn_fail(SEPATTN_EINVAL, "prefill: K/V not 16-byte aligned");
+  for (int i = 0; i < 3; ++i)
+    if (k_stride[i] < 0 || v_stride[i] < 0 || k_stride[i] % 8 != 0 || v_stride[i] % 8 != 0)
+      return sepattn_fail(SEPATTN_EINVAL, "prefill: strides must be non-negative multiples of 8 elements");
+  SEPATTN_TRY(sepattn_check_device());
+  return sepcache_launch_prefill(c, k, v, k_stride, v_stride, m, (hipStream_t)stream);
 }
 
 int sepcache_export_order(const sepcache* c, int32_t* pos, int32_t* len, void* stream) {

@@ -175,6 +175,99 @@ __global__ void reset_kernel(CacheParams p) {
   if (threadIdx.x < 8) p.state[bh * 8 + threadIdx.x] = 0;
 }
 
+// Seeds one (stream, KV head) with the state that L pushes from empty leave:
+// a prompt handed over from prefill.  Every slot's content is a closed form
+// of L.  Ring token j (token a + j) always goes to ring slot j mod W (each
+// append goes to head + count, which departures leave unchanged), and
+// separator push i to ring slot i mod s; the queue holds its last Lq tokens
+// and the separator ring the last min(s, cnt) of the cnt separators that
+// left the queue.  A ring slot that holds no entry keeps the K/V of its last
+// occupant (departures clear only the slot's metadata); other empty slots
+// were never written since the reset and hold zeros.
+constexpr int PF_THREADS = 256, PF_PER_THREAD = 4, PF_CHUNKS = PF_THREADS * PF_PER_THREAD;
+
+__global__ __launch_bounds__(PF_THREADS) void prefill_kernel(CacheParams p, const bf16* k, const bf16* v, int64_t ksb,
+                                                      int64_t ksh, int64_t kst, int64_t vsb, int64_t vsh,
+                                                      int64_t vst, int L, const uint8_t* is_sep,
+                                                      const int32_t* sep_idx, const int32_t* sep_before) {
+  const int bh = blockIdx.x, b = bh / p.Hkv, h = bh % p.Hkv;
+  const int W = p.n + 1, P = p.P, n = p.n - p.P, NCH = p.d / 8;
+  const int x = max(0, L - p.a);  // tokens that entered the queue
+  const int Lq = x <= n + P ? x : n + (x - n - P - 1) % (P + 1);
+  const int cnt = sep_before[(size_t)b * (L + 1) + (L - Lq)];  // separators that left it
+  const int sepc = min(p.s, cnt);
+  const uint8_t* fl = is_sep + (size_t)b * L;
+  const int32_t* si = sep_idx + (size_t)b * L;
+  const bf16* kp = k + b * ksb + h * ksh;
+  const bf16* vp = v + b * vsb + h * vsh;
+  int32_t* spos = p.slot_pos + (size_t)bh * p.slots;
+  uint8_t* ssep = p.slot_sep + (size_t)bh * p.slots;
+  bf16* kc = p.k + (size_t)bh * p.slots * p.d;
+  bf16* vc = p.v + (size_t)bh * p.slots * p.d;
+  auto token_of = [&](int slot) -> int {
+    if (slot < p.a) return slot < L ? slot : -1;
+    if (slot < p.a + p.s) {
+      if (sepc == 0) return -1;
+      const int base = cnt - sepc;
+      const int i = base + ((slot - p.a - base) % p.s + p.s) % p.s;
+      return i < cnt ? si[i] : -1;
+    }
+    if (Lq == 0) return -1;
+    const int base = x - Lq;
+    const int j = base + ((slot - p.a - p.s - base) % W + W) % W;
+    return j < x ? p.a + j : -1;
+  };
+  // the token whose K/V a slot holds: its entry, or for an empty ring slot
+  // the last token that left it (the largest j < base congruent to it)
+  auto content_of = [&](int slot) -> int {
+    const int tok = token_of(slot);
+    if (tok >= 0 || slot < p.a + p.s) return tok;
+    const int base = x - Lq;
+    const int j = base - 1 - ((base - 1 - (slot - p.a - p.s)) % W + W) % W;
+    return j >= 0 ? p.a + j : -1;
+  };
+  // workgroup y of the pair's grid row takes chunks [y, y + 1) * PF_CHUNKS
+  // of the K/V rows (16 bytes each, PF_PER_THREAD per thread, all loads
+  // issued before the stores) and, the first, the metadata and counters
+  const int i0 = (int)blockIdx.y * PF_CHUNKS + (int)threadIdx.x;
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  u32x4 kx[PF_PER_THREAD], vx[PF_PER_THREAD];
+#pragma unroll
+  for (int u = 0; u < PF_PER_THREAD; ++u) {
+    const int i = i0 + u * PF_THREADS;
+    const int slot = i / NCH, ch = i % NCH;
+    const int tok = i < p.slots * NCH ? content_of(slot) : -1;
+    kx[u] = tok >= 0 ? ld16(kp + tok * kst + ch * 8) : z;
+    vx[u] = tok >= 0 ? ld16(vp + tok * vst + ch * 8) : z;
+  }
+#pragma unroll
+  for (int u = 0; u < PF_PER_THREAD; ++u) {
+    const int i = i0 + u * PF_THREADS;
+    if (i < p.slots * NCH) {
+      st16(kc + (size_t)(i / NCH) * p.d + (i % NCH) * 8, kx[u]);
+      st16(vc + (size_t)(i / NCH) * p.d + (i % NCH) * 8, vx[u]);
+    }
+  }
+  if (blockIdx.y != 0) return;
+  for (int slot = threadIdx.x; slot < p.slots; slot += blockDim.x) {
+    const int tok = token_of(slot);
+    spos[slot] = tok;
+    ssep[slot] = tok >= 0 ? fl[tok] : 0;
+  }
+  if (threadIdx.x == 0) {
+    Counters c;
+    c.t = L;
+    c.nsink = min(p.a, L);
+    c.seph = p.s > 0 ? max(0, cnt - p.s) % p.s : 0;
+    c.sepc = sepc;
+    c.winh = (x - Lq) % W;
+    c.winc = Lq;
+    c.flags = 0;
+    c.oldsep = Lq > 0 ? fl[p.a + x - Lq] : 0;
+    store_counters(p.state + (size_t)bh * 8, c);
+  }
+}
+
 // Copies one row (d elements of K and of V) with the workgroup's threads.
 __device__ __forceinline__ void copy_row(int d, const bf16* ks, const bf16* vs, bf16* kd, bf16* vd) {
   const int ch = d / 8;
@@ -1338,6 +1431,16 @@ AttendParams attend_params(const sepcache* c, int Hq, const void* q, float scale
 int sepcache_launch_reset(const sepcache* c, hipStream_t st) {
   hipLaunchKernelGGL(reset_kernel, dim3(c->B * c->Hkv), dim3(256), 0, st, make_params(c));
   return sepattn_hip_check(hipGetLastError(), "reset launch");
+}
+
+int sepcache_launch_prefill(const sepcache* c, const void* k, const void* v, const int64_t* ks, const int64_t* vs,
+                            const sepattn_mask* m, hipStream_t st) {
+  const CacheParams cp = make_params(c);
+  const int wgs = (cp.slots * (c->d / 8) + PF_CHUNKS - 1) / PF_CHUNKS;  // per (stream, KV head)
+  hipLaunchKernelGGL(prefill_kernel, dim3(c->B * c->Hkv, wgs), dim3(PF_THREADS), 0, st, cp, (const bf16*)k,
+                     (const bf16*)v, ks[0], ks[1], ks[2], vs[0], vs[1], vs[2], m->L, (const uint8_t*)m->is_sep,
+                     (const int32_t*)m->sep_idx, (const int32_t*)m->sep_before);
+  return sepattn_hip_check(hipGetLastError(), "prefill launch");
 }
 
 // With a past window, an append first flushes a full window queue.

@@ -117,3 +117,18 @@ def test_argument_validation_without_gpu():
     assert b"capacity" in lib.sepattn_last_error()
     c.c = 0
     assert lib.sepcache_step(ctypes.byref(c), None, p, p, 4, p, 0.1, 1, p, None, 0, None) == _lib.EINVAL
+    # prompt hand-off: the mask must describe the cache's streams and sinks
+    st3 = (ctypes.c_int64 * 3)(0, 0, 64)
+    mk = _lib.SepattnMask()
+    assert lib.sepcache_prefill(ctypes.byref(c), p, p, st3, st3, None, None) == _lib.EINVAL
+    mk.B, mk.L, mk.a, mk.n = 2, 10, 4, 3
+    mk.is_sep = mk.sep_idx = mk.sep_before = mk.sep_cnt = mk.plain_idx = mk.plain_cnt = mk.kept = 4096
+    mk.a = 3
+    assert lib.sepcache_prefill(ctypes.byref(c), p, p, st3, st3, ctypes.byref(mk), None) == _lib.EINVAL
+    assert b"a=" in lib.sepattn_last_error()
+    mk.a, mk.B = 4, 3
+    assert lib.sepcache_prefill(ctypes.byref(c), p, p, st3, st3, ctypes.byref(mk), None) == _lib.EINVAL
+    mk.B = 2
+    assert lib.sepcache_prefill(ctypes.byref(c), None, p, st3, st3, ctypes.byref(mk), None) == _lib.EINVAL
+    bad = (ctypes.c_int64 * 3)(0, 0, 65)
+    assert lib.sepcache_prefill(ctypes.byref(c), p, p, bad, st3, ctypes.byref(mk), None) == _lib.EINVAL
