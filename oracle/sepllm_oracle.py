@@ -61,6 +61,17 @@ def separator_flags(tok: np.ndarray, sep_ids) -> np.ndarray:
     return np.isin(np.asarray(tok), np.asarray(list(sep_ids))).astype(np.uint8)
 
 
+def fixed_flags(B: int, L: int, delta: int) -> np.ndarray:
+    """FixLLM anchors, [HUB] third reviewer A2: every delta-th token is kept
+    outside the neighbouring window, in place of the separators.  Read as the
+    delta-th, 2*delta-th, ... token counting from one: f[b, j] = 1 iff delta
+    divides j + 1, for every sequence."""
+    if delta < 1:
+        raise ValueError("delta >= 1")
+    j = np.arange(L)
+    return np.ascontiguousarray(np.broadcast_to(((j + 1) % delta == 0).astype(np.uint8), (B, L)))
+
+
 def mask_rows(f_b: np.ndarray, a: int, n: int, r0: int, r1: int, c1: int | None = None) -> np.ndarray:
     """Rows [r0, r1) of the SepLLM mask of one sequence, columns [0, c1).
 

@@ -84,6 +84,24 @@ def test_mask_window_covering_sequence_is_causal():
     assert np.array_equal(M, np.broadcast_to(np.tril(np.ones((50, 50), bool)), M.shape))
 
 
+def test_fixed_anchors():
+    """FixLLM flags ([HUB] third reviewer A2): the tokens numbered delta,
+    2 delta, ... from one, by stepping; delta = 1 makes every token an anchor
+    (the mask is causal); delta > L leaves none (sinks + window, StreamingLLM)."""
+    for delta in range(1, 8):
+        for L in range(1, 31):
+            f = orc.fixed_flags(2, L, delta)
+            want = np.zeros(L, dtype=np.uint8)
+            want[list(range(delta - 1, L, delta))] = 1
+            assert np.array_equal(f[0], want) and np.array_equal(f[1], want), (delta, L)
+    L, a, n = 40, 3, 5
+    M = orc.mask_dense(orc.fixed_flags(1, L, 1), a, n)[0]
+    assert np.array_equal(M, np.tril(np.ones((L, L), bool)))
+    M = orc.mask_dense(orc.fixed_flags(1, L, L + 1), a, n)[0]
+    for i in range(L):
+        assert set(np.nonzero(M[i])[0].tolist()) == set(range(min(a, i + 1))) | set(range(max(0, i - n + 1), i + 1))
+
+
 def _kept_closed_form(f_b, a, n):
     """Per row i: min(i+1, a) sinks, the window positions in [max(a, i-n+1), i],
     and the separators >= a that lie before the window."""
