@@ -201,6 +201,35 @@ def measured_traffic() -> dict:
     return out if sha == kernel_sources_sha256() else {}
 
 
+def fixllm_leg(pre: PrefillLeg, delta: int, reps: int) -> dict:
+    """The prefill forward and backward with fixed-interval anchors (FixLLM:
+    one anchor every delta tokens in place of the separators) on the prefill
+    leg's own tensors, event-timed; kept-FLOP rates as for the separator mask."""
+    wl = pre.wl
+    m = sa.build_mask_fixed(wl.B, wl.L, delta, wl.a, wl.n)
+    o, lse = sa.sepattn_fwd(pre.q, pre.k, pre.v, m, pre.scale)
+    sa.sepattn_bwd(pre.q, pre.k, pre.v, o, lse, pre.do, m, pre.scale, workspace=pre.ws)
+    torch.cuda.synchronize()
+    kept = int(m.kept.sum().cpu())
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tf = tb = 0.0
+    for _ in range(reps):
+        e[0].record()
+        sa.sepattn_fwd(pre.q, pre.k, pre.v, m, pre.scale, out=o, lse=lse)
+        e[1].record()
+        sa.sepattn_bwd(pre.q, pre.k, pre.v, o, lse, pre.do, m, pre.scale, workspace=pre.ws)
+        e[2].record()
+        torch.cuda.synchronize()
+        tf += e[0].elapsed_time(e[1])
+        tb += e[1].elapsed_time(e[2])
+    tf, tb = tf / reps, tb / reps
+    fwd = 4.0 * wl.d * kept * wl.Hq / (tf * 1e-3) / 1e12
+    bwd = 10.0 * wl.d * kept * wl.Hq / (tb * 1e-3) / 1e12
+    return {"delta": delta, "kept_pairs_per_head": kept, "fwd_ms": round(tf, 4), "bwd_ms": round(tb, 4),
+            "fwd_tflops": round(fwd, 2), "bwd_tflops": round(bwd, 2),
+            "fwd_util": round(fwd / PEAK_BF16_TFLOPS, 4), "bwd_util": round(bwd / PEAK_BF16_TFLOPS, 4)}
+
+
 def handoff_leg(wl: synth.DecodeWorkload, L: int, seed: int, reps: int = 50) -> dict:
     """sepcache_prefill of an L-token prompt into one layer's caches.  Its
     algorithmic bytes: the K/V rows of the entries kept (read once) and every
@@ -245,6 +274,8 @@ def main():
     ap.add_argument("--general-tokens", type=int, default=4096,
                     help="tokens of the capacity-800 cache leg (the pages' streaming capacity; 0 skips it)")
     ap.add_argument("--general-layers", type=int, default=8, help="layer caches of that leg")
+    ap.add_argument("--fixllm-delta", type=int, default=8,
+                    help="anchor interval of the FixLLM prefill leg (0 skips it)")
     ap.add_argument("--handoff-tokens", type=int, default=4096,
                     help="prompt length of the prefill-to-cache hand-off leg (0 skips it)")
     ap.add_argument("--seed", type=int, default=0)
@@ -308,6 +339,7 @@ def main():
         del gen
     # Prompt hand-off: seed the Llama decode caches (16 streams x 8 KV heads,
     # 324 entries) from a prompt's K/V and mask metadata, timed on its own.
+    fix_out = fixllm_leg(pre, args.fixllm_delta, args.steps) if args.fixllm_delta > 0 else None
     hand_out = None
     if args.handoff_tokens > 0:
         hand_out = handoff_leg(synth.LLAMA_DECODE, args.handoff_tokens, args.seed)
@@ -361,6 +393,8 @@ def main():
         out["decode_c800"] = gen_out
     if hand_out is not None:
         out["prefill_handoff"] = hand_out
+    if fix_out is not None:
+        out["prefill_fixllm"] = fix_out
     traffic = measured_traffic()
     dec_launch_us = t_dec * 1e3 / (dec.wl.T * args.layers)
     per_launch_bytes = dec.bytes / (dec.wl.T * args.layers)

@@ -100,6 +100,14 @@ SEPATTN_API int sepattn_mask_carve(sepattn_mask* m, int B, int L, int a, int n, 
 SEPATTN_API int sepattn_build_mask(const int32_t* tok, const int32_t* sep_ids, int n_sep,
                        const sepattn_mask* m, void* stream);
 
+/* The same metadata with fixed-interval anchors in place of separators
+ * (FixLLM, [HUB] third reviewer A2: every delta-th token is kept outside the
+ * window): f[b, j] = 1 iff (j + 1) mod delta == 0, for every sequence; n and
+ * a as for sepattn_build_mask.  A subset of the separators is the other
+ * anchor-set variant ([HUB] first reviewer A6): sepattn_build_mask with
+ * those ids.  delta >= 1.  One launch. */
+SEPATTN_API int sepattn_build_mask_fixed(int delta, const sepattn_mask* m, void* stream);
+
 /* Expand the metadata into the dense mask, bit-packed: bits[b][i][w] holds
  * M[b,i,32w+t] in bit t, for w < ceil(L/32); bits past L are 0.  The kernel
  * walks each row the way the forward kernel does (gathered anchors, then the

@@ -54,6 +54,7 @@ _SIGS = {
     "sepcache_decode": (c_int, [POINTER(SepCacheStruct), c_int, c_void_p, c_float, c_int, c_void_p,
                                 c_void_p, c_size_t, c_void_p]),
     "sepcache_export_order": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, c_void_p]),
+    "sepattn_build_mask_fixed": (c_int, [c_int, POINTER(SepattnMask), c_void_p]),
     "sepcache_prefill": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, POINTER(c_int64), POINTER(c_int64),
                                  POINTER(SepattnMask), c_void_p]),
     "sepcache_step": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_float,

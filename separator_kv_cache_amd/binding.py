@@ -71,6 +71,14 @@ def build_mask(tok: torch.Tensor, sep_ids, a: int, n: int) -> Mask:
     return m
 
 
+def build_mask_fixed(B: int, L: int, delta: int, a: int, n: int, device="cuda") -> Mask:
+    """sepattn_build_mask_fixed: fixed-interval anchors, token j kept outside
+    the window iff (j + 1) % delta == 0."""
+    m = Mask(B, L, a, n, device)
+    check(_lib.load().sepattn_build_mask_fixed(int(delta), ctypes.byref(m.c), _stream()))
+    return m
+
+
 def mask_bits(m: Mask) -> torch.Tensor:
     """sepattn_mask_bits: the dense mask as uint32 words [B, L, ceil(L/32)]
     (int32 storage holding the same bits)."""

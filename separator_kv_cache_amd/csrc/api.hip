@@ -12,6 +12,7 @@
 #include "traverse.h"
 
 // kernel launchers (mask.hip, fwd.hip, bwd.hip, cache.hip)
+int sepattn_launch_build_mask_fixed(int delta, const sepattn_mask* m, hipStream_t st);
 int sepattn_launch_build_mask(const int32_t* tok, const int32_t* ids, int n_ids, const sepattn_mask* m,
                               hipStream_t st);
 int sepattn_launch_mask_bits(const sepattn_mask* m, uint32_t* bits, hipStream_t st);
@@ -116,6 +117,14 @@ int sepattn_build_mask(const int32_t* tok, const int32_t* sep_ids, int n_sep, co
     return sepattn_fail(SEPATTN_EINVAL, "build_mask: n_sep=%d not in [1, %d]", n_sep, SEPATTN_MAX_SEP_IDS);
   SEPATTN_TRY(sepattn_check_device());
   return sepattn_launch_build_mask(tok, sep_ids, n_sep, m, (hipStream_t)stream);
+}
+
+int sepattn_build_mask_fixed(int delta, const sepattn_mask* m, void* stream) {
+  g_err[0] = 0;
+  SEPATTN_TRY(check_mask(m, "build_mask_fixed"));
+  if (delta < 1) return sepattn_fail(SEPATTN_EINVAL, "build_mask_fixed: delta=%d < 1", delta);
+  SEPATTN_TRY(sepattn_check_device());
+  return sepattn_launch_build_mask_fixed(delta, m, (hipStream_t)stream);
 }
 
 int sepattn_mask_bits(const sepattn_mask* m, uint32_t* bits, void* stream) {

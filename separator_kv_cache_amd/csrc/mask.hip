@@ -62,19 +62,22 @@ __device__ long long block_sum64(long long v) {
   return s;
 }
 
+// Anchor flags: token j is a separator (its id is in ids) or, with every > 0,
+// j is one of the fixed-interval anchors (j + 1) mod every == 0 (tok unused).
 __global__ __launch_bounds__(kScanThreads) void build_mask_kernel(
-    const int32_t* __restrict__ tok, SepIds ids, int L, int a, int n,
+    const int32_t* __restrict__ tok, SepIds ids, int every, int L, int a, int n,
     uint8_t* __restrict__ is_sep, int32_t* __restrict__ sep_idx, int32_t* __restrict__ sep_before,
     int32_t* __restrict__ sep_cnt, int32_t* __restrict__ plain_idx, int32_t* __restrict__ plain_cnt,
     int64_t* __restrict__ kept) {
   const int b = blockIdx.x;
   const int per = (L + kScanThreads - 1) / kScanThreads;
   const int p0 = min(L, (int)threadIdx.x * per), p1 = min(L, p0 + per);
-  const int32_t* tk = tok + (size_t)b * L;
+  const int32_t* tk = every > 0 ? nullptr : tok + (size_t)b * L;
+  auto flag = [&](int j) { return every > 0 ? (j + 1) % every == 0 : is_separator(tk[j], ids); };
 
   int cs = 0, cp = 0;
   for (int j = p0; j < p1; ++j) {
-    const bool f = is_separator(tk[j], ids);
+    const bool f = flag(j);
     is_sep[(size_t)b * L + j] = f ? 1 : 0;
     if (j >= a) {
       cs += f ? 1 : 0;
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(kScanThreads) void build_mask_kernel(
   int32_t* pi = plain_idx + (size_t)b * L;
   long long kl = 0;
   for (int j = p0; j < p1; ++j) {
-    const bool f = is_separator(tk[j], ids);
+    const bool f = flag(j);
     sb[j] = os;
     // kept pairs of row j: its sinks and its window positions past the
     // sinks ...
@@ -145,10 +148,20 @@ int sepattn_launch_build_mask(const int32_t* tok, const int32_t* ids, int n_ids,
   SepIds s;
   s.n = n_ids;
   for (int k = 0; k < SEPATTN_MAX_SEP_IDS; ++k) s.id[k] = k < n_ids ? ids[k] : 0;
-  hipLaunchKernelGGL(build_mask_kernel, dim3(m->B), dim3(kScanThreads), 0, st, tok, s, m->L, m->a, m->n,
+  hipLaunchKernelGGL(build_mask_kernel, dim3(m->B), dim3(kScanThreads), 0, st, tok, s, 0, m->L, m->a, m->n,
                      m->is_sep, m->sep_idx, m->sep_before, m->sep_cnt, m->plain_idx, m->plain_cnt,
                      m->kept);
   return sepattn_hip_check(hipGetLastError(), "build_mask launch");
+}
+
+int sepattn_launch_build_mask_fixed(int delta, const sepattn_mask* m, hipStream_t st) {
+  SepIds s;
+  s.n = 0;
+  for (int k = 0; k < SEPATTN_MAX_SEP_IDS; ++k) s.id[k] = 0;
+  hipLaunchKernelGGL(build_mask_kernel, dim3(m->B), dim3(kScanThreads), 0, st, (const int32_t*)nullptr, s, delta,
+                     m->L, m->a, m->n, m->is_sep, m->sep_idx, m->sep_before, m->sep_cnt, m->plain_idx,
+                     m->plain_cnt, m->kept);
+  return sepattn_hip_check(hipGetLastError(), "build_mask_fixed launch");
 }
 
 int sepattn_launch_mask_bits(const sepattn_mask* m, uint32_t* bits, hipStream_t st) {
