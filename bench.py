@@ -274,6 +274,8 @@ def main():
     ap.add_argument("--general-tokens", type=int, default=4096,
                     help="tokens of the capacity-800 cache leg (the pages' streaming capacity; 0 skips it)")
     ap.add_argument("--general-layers", type=int, default=8, help="layer caches of that leg")
+    ap.add_argument("--resident-tokens", type=int, default=2048,
+                    help="tokens of the one-layer (cache-resident) decode leg (0 skips it)")
     ap.add_argument("--fixllm-delta", type=int, default=8,
                     help="anchor interval of the FixLLM prefill leg (0 skips it)")
     ap.add_argument("--handoff-tokens", type=int, default=4096,
@@ -316,6 +318,24 @@ def main():
         t_dec += dec.time_ms()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # The same decode with one layer's caches (21 MB, resident in the 256 MB
+    # Infinity Cache between tokens), beside the 32-layer figure above.
+    res_out = None
+    if args.resident_tokens > 0:
+        res = DecodeLeg(dwl.with_(T=args.resident_tokens), 1, args.seed)
+        res.step()
+        torch.cuda.synchronize()
+        t_res = 0.0
+        for _ in range(args.steps):
+            res.step()
+            torch.cuda.synchronize()
+            t_res += res.time_ms()
+        t_res /= args.steps
+        gbs = res.bytes / (t_res * 1e-3) / 1e9
+        res_out = {"layers": 1, "tokens": res.wl.T, "ms": round(t_res, 3), "gbs": round(gbs, 1),
+                   "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                   "us_per_token_layer": round(t_res * 1e3 / res.wl.T, 3)}
+        del res
     # The four-block cache at capacity c = 800 (a past window of 476 entries)
     # on the same decode geometry: timed on its own, outside the step.
     gen_out = None
@@ -389,6 +409,8 @@ def main():
         "roofline": None,
         "rooflines": None,
     }
+    if res_out is not None:
+        out["decode_resident"] = res_out
     if gen_out is not None:
         out["decode_c800"] = gen_out
     if hand_out is not None:
