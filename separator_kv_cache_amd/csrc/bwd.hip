@@ -13,6 +13,8 @@
 //    keys of one class and walks the rows that can see them: [first key, L)
 //    for anchors, [first key, last key + n) for plain keys, summing over the
 //    q heads of its KV head.
+#include <type_traits>
+
 #include "common.h"
 #include "traverse.h"
 
@@ -217,24 +219,36 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
 //
 // Key-major: a workgroup of 8 waves owns KT = 128 keys of one class and walks
 // the rows that see them in blocks of RB = 64 rows, for each q head of its KV
-// head in turn (iteration it = row block * group + head).  Waves 2kg and
-// 2kg + 1 own the same 32 keys (key group kg).  Per block, the wave with
-// hf = w % 2 forms S = Q K^T and dP = dO V^T for the rows [32 hf, 32 hf + 32)
-// and from them P and dS, which the two waves exchange through LDS (phase
-// A); then it accumulates dV^T += dO^T P and dK^T += Q^T dS over all 64 rows
-// for the head dims [D/2 hf, D/2 hf + D/2) (phase B).  No MFMA work is
-// duplicated, and a wave keeps K, V of its keys for all dims but dK, dV for
-// half of them, which fits two waves per SIMD.
+// head in turn (iteration j = row block * group + head).  Waves 2kg and
+// 2kg + 1 own the same 32 keys (key group kg); the wave with hf = w % 2 forms
+// S = Q K^T and dP = dO V^T for the rows [32 hf, 32 hf + 32) and from them P
+// and dS, which the two waves exchange through LDS; each then accumulates
+// dV^T += dO^T P and dK^T += Q^T dS over all 64 rows for the head dims
+// [D/2 hf, D/2 hf + D/2).  No MFMA work is duplicated, and a wave keeps K, V
+// of its keys for all dims but dK, dV for half of them, which fits two waves
+// per SIMD.
 //
-// The two waves on a SIMD (w and w + 4) belong to different key-group
-// pairs, and the second half of the workgroup runs one phase behind the
-// first (one extra barrier), so while one wave exponentiates in phase A the
-// other keeps the matrix core busy in phase B.  Every wave runs A(it),
-// barrier, B(it), barrier.  Tile it + 1 of Q/dO is written over tile it - 1
-// in the interval where the first half runs B(it) and the second half A(it)
-// (both halves store from those phases), and the loads of tile it + 2 start
-// there; tile it - 1 was last read by the second half's B(it - 1), one
-// interval earlier.
+// Every wave alternates a matrix phase M(j) (the MFMAs of S, dP for block
+// j + 1 and of dV, dK for block j) and a vector phase V(j) (P and dS of block
+// j from the scores M(j - 1) left in registers, written to LDS), with a
+// workgroup barrier after each.  The two waves on a SIMD (w and w + 4) are in
+// different halves of the workgroup, and the second half runs one phase
+// behind the first, so at any time one wave of a SIMD issues only MFMAs (at
+// raised priority) while the other issues only vector work.  Both waves of a
+// key-group pair are in the same half, so their exchange sits between V(j)
+// and M(j) of that half.
+//
+// Q/dO tiles (with lse and D of their rows) rotate through three LDS buffers:
+// tile j is read from M(j - 1) of the first half to M(j) of the second.  Each
+// half moves its own 32 rows of a tile (global -> registers -> LDS): the
+// first half stores rows [0, 32) of tile j + 1 in its V(j), the second half
+// rows [32, 64) of tile j + 2 in its V(j), which falls between the last read
+// of the buffer's previous tile and the first read of the new one.  Each
+// half issues the loads of its next rows from inside the following M phase,
+// between its first MFMAs: there the address arithmetic and the load issue
+// run beside the matrix core instead of in front of it (measured: issuing
+// them at the head of either phase put several hundred cycles on the
+// critical path of every interval).
 
 // Q/dO tiles of dK/dV are read by rows (16 lanes, one 16-byte chunk of 16
 // consecutive rows) and by transposing reads (32 lanes, 8 bytes of 4
@@ -252,25 +266,29 @@ struct DkvLayout {
   __device__ static int tau(int r) { return SWZ ? (r >> 2) & 3 : 0; }
   static constexpr int T_BYTES = RB * STR * 2;                // one Q or dO tile
   static constexpr int BUF_BYTES = 2 * T_BYTES + 2 * RB * 4;  // Q, dO, lse2, D
+  static constexpr int NBUF = 3;
   static constexpr int PSTR = RB + 8;                         // P/dS: row stride per key (elements)
   static constexpr int X_BYTES = 128 * PSTR * 2;              // P or dS of the 128 keys
-  static constexpr int SMEM = 2 * BUF_BYTES + 2 * X_BYTES;
+  static constexpr int SMEM = NBUF * BUF_BYTES + 2 * X_BYTES;
+  static_assert(SMEM <= 160 * 1024, "dK/dV tiles exceed the LDS of a workgroup");
 };
 
 template <int D>
 __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
   using LY = DkvLayout<D>;
-  constexpr int NT = 512, KT = 128, STR = LY::STR, PSTR = LY::PSTR;
+  constexpr int KT = 128, STR = LY::STR, PSTR = LY::PSTR;
   constexpr int NKK = D / 16;          // 16-dim steps of S and dP
   constexpr int HD = D / 2;            // head dims whose dK, dV a wave accumulates
   constexpr int NDBH = HD / 32;        // 32-dim blocks of them
   constexpr int CH = D / 8;            // 16-byte chunks per row
-  constexpr int PT = RB * CH / NT;     // tile chunks per thread (Q and dO each)
-  static_assert(PT * NT == RB * CH, "tile chunks must divide the workgroup");
+  constexpr int HT = 256;              // threads of a half
+  constexpr int PT = (RB / 2) * CH / HT;  // chunks per thread of a half tile (Q and dO each)
+  static_assert(PT * HT == (RB / 2) * CH, "half-tile chunks must divide the half workgroup");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = wave >> 1, hf = wave & 1, half = wave >> 2;
+  const int ht = (int)threadIdx.x & (HT - 1);
   // XCD-aware order (as tile_work): the key tiles of one (sequence, KV head)
   // run on one XCD, anchor tiles (the longest row ranges) first.  (Spreading
   // one head over all XCDs instead, to share the Infinity Cache, measured
@@ -322,106 +340,172 @@ __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
   // not change what they share.)
   const int rs_first = anchors ? j_first + RB * (n_rb - 1) : j_first;
   const int rs_step = anchors ? -RB : RB;
+  // LDS: P and dS first, then the three tile buffers, so that every access is
+  // a per-lane base plus an offset below 64 KiB
+  char* xp = smem;              // P of the 128 keys, [key][row]
+  char* xd = xp + LY::X_BYTES;  // dS
+  // (unsigned offsets, so that constant parts fold into the LDS instructions)
+  auto tbuf_off = [&](int j) -> uint32_t {  // j >= -1
+    return 2u * LY::X_BYTES + ((uint32_t)(j + LY::NBUF) % (uint32_t)LY::NBUF) * (uint32_t)LY::BUF_BYTES;
+  };
+  // A lane's LDS address in tile buffer j: its own offset plus the buffer's,
+  // made opaque so that the compiler adds the constant parts of each access
+  // as instruction offsets instead of keeping one register per access.
+  auto at_buf = [&](int j, uint32_t lane_off) -> char* {
+    uint32_t o = tbuf_off(j) + lane_off;
+    asm volatile("" : "+v"(o));
+    return smem + o;
+  };
 
-  // ---- Q/dO row tiles: global -> registers -> LDS.  Thread x moves chunk
-  // x % CH of rows x / CH + u * (NT / CH); rows past L load as zeros and get
-  // lse2 = +inf, so their P is exactly 0.
+  // ---- this half's 32 rows of a Q/dO tile: global -> registers -> LDS.
+  // Thread x of the half moves chunk x % CH of rows 32 half + x / CH +
+  // u * (HT / CH); rows past L load as zeros and get lse2 = +inf, so their P
+  // is exactly 0.  fetch_half() is called for tiles 0, 1, 2, ... in order:
+  // (row block, head) of the next call advance as counters.
   u32x4 qr[PT], dr[PT];
   float lse_r = 0.f, d_r = 0.f;
   bool lse_ok = false;
-  // fetch() is called for it = 0, 1, 2, ... in order: (row block, head) of
-  // the next call advance as counters instead of divisions.
   int f_rs = rs_first, f_h = kvh * group;
-  auto fetch = [&](int it) {
+  auto fetch_half = [&](int j) {
     // (uniform values; readfirstlane keeps the buffer resources in scalar
     // registers, else each load becomes a loop over distinct descriptors)
     const int rs = __builtin_amdgcn_readfirstlane(f_rs), h = __builtin_amdgcn_readfirstlane(f_h);
-    const bool live = it < n_it;
+    const bool live = j < n_it;
     if (++f_h == (kvh + 1) * group) { f_h = kvh * group; f_rs += rs_step; }
     const rsrc_t qrs = make_rsrc(p.q + b * p.sq[0] + h * p.sq[1], p.q_span);
     const rsrc_t drs = make_rsrc(p.dout + b * p.so[0] + h * p.so[1], p.o_span);
     const uint32_t qrow = (uint32_t)(p.sq[2] * 2), orow = (uint32_t)(p.so[2] * 2);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      const int i = rs + (int)threadIdx.x / CH + u * (NT / CH);
+      const int i = rs + 32 * half + ht / CH + u * (HT / CH);
       const bool ok = live && i < p.L;
-      const uint32_t c16 = ((int)threadIdx.x % CH) * 16;
+      const uint32_t c16 = (ht % CH) * 16;
       qr[u] = bld16(qrs, ok ? (uint32_t)i * qrow + c16 : BUF_OOB);
       dr[u] = bld16(drs, ok ? (uint32_t)i * orow + c16 : BUF_OOB);
     }
-    if (threadIdx.x < RB) {
+    if (ht < 32) {
       const size_t rowb = ((size_t)b * p.Hq + h) * p.L;
       const rsrc_t lrs = make_rsrc(p.lse + rowb, (uint32_t)p.L * 4u);
       const rsrc_t srs = make_rsrc(p.dsum + rowb, (uint32_t)p.L * 4u);
-      const int i = rs + (int)threadIdx.x;
+      const int i = rs + 32 * half + ht;
       lse_ok = live && i < p.L;
       const uint32_t off = lse_ok ? (uint32_t)i * 4u : BUF_OOB;
       lse_r = __builtin_bit_cast(float, bld4(lrs, off));
       d_r = __builtin_bit_cast(float, bld4(srs, off));
     }
   };
-  auto tbuf = [&](int it) -> uint32_t { return ((uint32_t)it & 1u) * (uint32_t)LY::BUF_BYTES; };
-  auto store = [&](int it) {
-    char* buf = smem + tbuf(it);
+  // (row 32 half + ht / CH + u (HT / CH) has tau of ht / CH + u (HT / CH):
+  // HT / CH is a multiple of 16 at d = 128)
+  const uint32_t st_off = (uint32_t)((32 * half + ht / CH) * STR * 2 + ((ht % CH) ^ LY::tau(ht / CH)) * 16);
+  auto store_half = [&](int j) {
+    char* buf = at_buf(j, st_off);
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-      const int r = (int)threadIdx.x / CH + u * (NT / CH), c = (int)threadIdx.x % CH;
-      const int at = r * STR * 2 + (c ^ LY::tau(r)) * 16;
-      st16(buf + at, qr[u]);
-      st16(buf + LY::T_BYTES + at, dr[u]);
+      st16(buf + u * (HT / CH) * STR * 2, qr[u]);
+      st16(buf + LY::T_BYTES + u * (HT / CH) * STR * 2, dr[u]);
     }
-    if (threadIdx.x < RB) {
-      float* ls = (float*)(buf + 2 * LY::T_BYTES);
-      const bool ok = lse_ok;
-      ls[threadIdx.x] = ok ? lse_r * 1.4426950408889634f : INFINITY;
-      ls[RB + threadIdx.x] = ok ? d_r : 0.f;
+    if (ht < 32) {
+      float* ls = (float*)(smem + tbuf_off(j) + 2 * LY::T_BYTES);
+      ls[32 * half + ht] = lse_ok ? lse_r * 1.4426950408889634f : INFINITY;
+      ls[RB + 32 * half + ht] = lse_ok ? d_r : 0.f;
     }
   };
 
-  char* xp = smem + 2 * LY::BUF_BYTES;        // P of the 128 keys, [key][row]
-  char* xd = xp + LY::X_BYTES;                // dS
   f32x16 dkacc[NDBH], dvacc[NDBH];
 #pragma unroll
   for (int db = 0; db < NDBH; ++db) { dkacc[db] = f32x16{}; dvacc[db] = f32x16{}; }
+  f32x16 sacc, dpacc;  // S, dP of the next block, from M(j - 1) to V(j)
   const int g = lane >> 4, li = lane & 15;
 
-  // ---- phase A(it): S, dP for rows [32 hf, 32 hf + 32) x this lane's key
-  // (lane = key; S and dP alternate so that consecutive MFMAs are
-  // independent, operand reads PD ahead), then P = exp2(scale_log2 S - lse2)
-  // on the rows that see the key and dS = P (dP - D); register r holds local
-  // row 32 hf + 8(r/4) + 4 hh + r%4.  P, dS go to LDS per key in the order
-  // the row contraction consumes them: its B slot s of a lane with
-  // hh = l/32 must hold row 16c + 8(s/4) + 4 hh + s%4 (the row the
-  // transposing read puts in A slot s), so within each 16-row chunk the rows
-  // are stored as 0-3, 8-11, 4-7, 12-15 and a lane reads its 8 values at
-  // position 16c + 8 hh with one 16-byte read.
-  int a_rs = rs_first, a_h = 0;  // row block of the next phase_a call (called for it = 0, 1, ...)
-  auto phase_a = [&](int it) {
-    const char* buf = smem + tbuf(it);
-    const int rs = a_rs;
-    if (++a_h == group) { a_h = 0; a_rs += rs_step; }
-    constexpr int NS = 2 * NKK, PD = 4;
-    // row 32 hf + qn, chunk c = 2 (i >> 1) + hh at position
-    // 4 (c >> 2) + ((c & 3) ^ tau): two bases, by bit 1 of c
-    const char* row = buf + (32 * hf + qn) * STR * 2;
-    const int ta = LY::tau(32 * hf + qn);
-    const char* base0 = row + ((hh ^ ta) * 16);
-    const char* base1 = row + (((2 + hh) ^ ta) * 16);
+  // ---- matrix phase M(j): with WITH_DKV, dV^T += dO^T P and dK^T += Q^T dS
+  // over the 64 rows of block j for head dims [HD hf, HD hf + HD): A through
+  // transposing reads of the tile, B = P, dS of this key group (lane l: key
+  // l % 32, the 8 rows at position 16c + 8(l / 32)); then S, dP for rows
+  // [32 hf, 32 hf + 32) of block j + 1 x this lane's key (lane = key; S and
+  // dP alternate so that consecutive MFMAs are independent).  One stream of
+  // MFMAs whose LDS operand reads run PD MFMAs ahead; the scores come last,
+  // so their accumulators are not live beside those of the dV, dK part.  On
+  // the last block the scores of the (absent) next block are formed from
+  // whatever the buffer holds and never used.
+  constexpr int NS = 2 * NKK, NB = (RB / 16) * NDBH * 2, PD = 4;
+  const int r0 = 4 * (g >> 1) + (li >> 2);
+  const int clo = 2 * (g & 1) + ((li & 3) >> 1);
+  const uint32_t tr_lo = (uint32_t)(r0 * STR * 2 + HD * hf * 2 + ((clo ^ LY::tau(r0)) * 16) + 8 * (li & 1));
+  const uint32_t tr_hi = (uint32_t)((r0 + 8) * STR * 2 + HD * hf * 2 + ((clo ^ LY::tau(r0 + 8)) * 16) + 8 * (li & 1));
+  const int ta = LY::tau(32 * hf + qn);
+  const uint32_t rd0 = (uint32_t)((32 * hf + qn) * STR * 2 + ((hh ^ ta) * 16));
+  const uint32_t rd1 = (uint32_t)((32 * hf + qn) * STR * 2 + (((2 + hh) ^ ta) * 16));
+  auto matrix_phase = [&](auto with_dkv, int j, int fetch_j) {
+    constexpr bool DKV = decltype(with_dkv)::value;
+    constexpr int N0 = DKV ? NB : 0, NM = N0 + NS;
+    // dV, dK operands: row 4 (g >> 1) + (li >> 2) (+ 8 for the upper half,
+    // + 16 c), column HD hf + 16 (g & 1) + 4 (li & 3) (+ 32 db) of tile j
+    const char* abase_lo = at_buf(j, tr_lo);
+    const char* abase_hi = at_buf(j, tr_hi);
+    const char* pb = xp + ((kg * 32 + qn) * PSTR + 8 * hh) * 2;
+    const char* sb = xd + ((kg * 32 + qn) * PSTR + 8 * hh) * 2;
+    // S, dP operands: row 32 hf + qn of tile j + 1, chunk c = 2 (i >> 1) + hh
+    // at position 4 (c >> 2) + ((c & 3) ^ tau): two bases, by bit 1 of c
+    const char* base0 = at_buf(j + 1, rd0);
+    const char* base1 = at_buf(j + 1, rd1);
+    // MFMA i < N0: chunk i / (2 NDBH), block (i >> 1) % NDBH, dV (even) / dK
+    // (odd); i >= N0: k = i - N0 is S (even) / dP (odd) of dims 16 (k >> 1)
     auto opnd = [&](int i) -> bf16x8 {
-      const int k = i >> 1;
-      return *(const bf16x8*)(((k & 1) ? base1 : base0) + ((i & 1) ? LY::T_BYTES : 0) + (k >> 1) * 64);
+      if (i < N0) {
+        const int c = i / (2 * NDBH), db = (i >> 1) % NDBH;
+        const int off = ((i & 1) ? 0 : LY::T_BYTES) + (16 * c * STR + 32 * db) * 2;  // dO for dV, Q for dK
+        const bf16x4 lo4 = lds_read_tr16(abase_lo + off);
+        const bf16x4 hi4 = lds_read_tr16(abase_hi + off);
+        return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+      }
+      const int k = (i - N0) >> 1;
+      return *(const bf16x8*)(((k & 1) ? base1 : base0) + (((i - N0) & 1) ? LY::T_BYTES : 0) + (k >> 1) * 64);
     };
-    f32x16 sacc = f32x16{}, dpacc = f32x16{};
-    bf16x8 op[NS];
+    bf16x8 op[NM], bp[RB / 16], bs[RB / 16];
+    auto prefetch = [&](int i) {
+      op[i] = opnd(i);
+      if (i < N0 && i % (2 * NDBH) == 0) {  // first MFMA of a row chunk: its P and dS
+        const int c = i / (2 * NDBH);
+        bp[c] = *(const bf16x8*)(pb + 16 * c * 2);
+        bs[c] = *(const bf16x8*)(sb + 16 * c * 2);
+      }
+    };
 #pragma unroll
-    for (int i = 0; i < PD; ++i) op[i] = opnd(i);
+    for (int i = 0; i < PD; ++i) prefetch(i);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) {
-      if (i + PD < NS) op[i + PD] = opnd(i + PD);
-      if (i & 1) dpacc = mfma32x16(op[i], vreg[i >> 1], dpacc);
-      else sacc = mfma32x16(op[i], kreg[i >> 1], sacc);
+    for (int i = 0; i < NM; ++i) {
+      if (i + PD < NM) prefetch(i + PD);
+      if (DKV && i == 2) fetch_half(fetch_j);  // address work and issue beside the MFMAs
+      if (i == N0) {
+        sacc = f32x16{};
+        dpacc = f32x16{};
+      }
+      if (i < N0) {
+        const int c = i / (2 * NDBH), db = (i >> 1) % NDBH;
+        if (i & 1) dkacc[db] = mfma32x16(op[i], bs[c], dkacc[db]);
+        else dvacc[db] = mfma32x16(op[i], bp[c], dvacc[db]);
+      } else {
+        const int k = i - N0;
+        if (k & 1) dpacc = mfma32x16(op[i], vreg[k >> 1], dpacc);
+        else sacc = mfma32x16(op[i], kreg[k >> 1], sacc);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // ---- vector phase V(j): P = exp2(scale_log2 S - lse2) on the rows of
+  // block j that see the key, dS = P (dP - D); register r holds local row
+  // 32 hf + 8(r/4) + 4 hh + r%4.  P, dS go to LDS per key in the order the
+  // row contraction consumes them: its B slot s of a lane with hh = l/32
+  // must hold row 16c + 8(s/4) + 4 hh + s%4 (the row the transposing read
+  // puts in A slot s), so within each 16-row chunk the rows are stored as
+  // 0-3, 8-11, 4-7, 12-15 and a lane reads its 8 values at position
+  // 16c + 8 hh with one 16-byte read.
+  int v_rs = rs_first, v_h = 0;  // row block of the next vector_phase call (called for j = 0, 1, ...)
+  auto vector_phase = [&](int j) {
+    const char* buf = smem + tbuf_off(j);
+    const int rs = v_rs;
+    if (++v_h == group) { v_h = 0; v_rs += rs_step; }
     // lse2 and D of this lane's rows: four runs of 4 consecutive rows
     const float* ls = (const float*)(buf + 2 * LY::T_BYTES) + 32 * hf + 4 * hh;
     f32x4 l2[4], dd[4];
@@ -459,64 +543,26 @@ __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
     else pds(true);
   };
 
-  // ---- phase B(it): dV^T += dO^T P, dK^T += Q^T dS over the 64 rows for
-  // head dims [HD hf, HD hf + HD): A through transposing reads of the
-  // tiles, B = P, dS of this key group (lane l: key l % 32, the 8 rows at
-  // position 16c + 8(l / 32)); operand reads PD MFMAs ahead.
-  auto phase_b = [&](int it) {
-    const char* buf = smem + tbuf(it);
-    // row 4 (g >> 1) + (li >> 2) (+ 8 for the upper half, + 16 c), column
-    // HD hf + 16 (g & 1) + 4 (li & 3) (+ 32 db): the chunk's low two bits come
-    // from the lane and are XORed with tau of the row, the rest are immediates
-    const int r0 = 4 * (g >> 1) + (li >> 2);
-    const int clo = 2 * (g & 1) + ((li & 3) >> 1);
-    const char* abase_lo = buf + r0 * STR * 2 + HD * hf * 2 + ((clo ^ LY::tau(r0)) * 16) + 8 * (li & 1);
-    const char* abase_hi = buf + (r0 + 8) * STR * 2 + HD * hf * 2 + ((clo ^ LY::tau(r0 + 8)) * 16) + 8 * (li & 1);
-    const char* pb = xp + ((kg * 32 + qn) * PSTR + 8 * hh) * 2;
-    const char* sb = xd + ((kg * 32 + qn) * PSTR + 8 * hh) * 2;
-    constexpr int NB = (RB / 16) * NDBH * 2, PD = 4;  // MFMA i: chunk c, block db, dV (even) / dK (odd)
-    auto opnd = [&](int i) -> bf16x8 {
-      const int c = i / (2 * NDBH), db = (i >> 1) % NDBH;
-      const int off = ((i & 1) ? 0 : LY::T_BYTES) + (16 * c * STR + 32 * db) * 2;  // dO for dV, Q for dK
-      const bf16x4 lo4 = lds_read_tr16(abase_lo + off);
-      const bf16x4 hi4 = lds_read_tr16(abase_hi + off);
-      return bf16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-    };
-    auto bop = [&](int i) -> bf16x8 {
-      const int c = i / (2 * NDBH);
-      return *(const bf16x8*)(((i & 1) ? sb : pb) + 16 * c * 2);
-    };
-    bf16x8 op[NB], bo[NB];
-#pragma unroll
-    for (int i = 0; i < PD; ++i) { op[i] = opnd(i); bo[i] = bop(i); }
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if (i + PD < NB) { op[i + PD] = opnd(i + PD); bo[i + PD] = bop(i + PD); }
-      const int db = (i >> 1) % NDBH;
-      if (i & 1) dkacc[db] = mfma32x16(op[i], bo[i], dkacc[db]);
-      else dvacc[db] = mfma32x16(op[i], bo[i], dvacc[db]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  fetch(0);
-  store(0);
-  fetch(1);
+  // ---- prologue: tile 0 and rows [32, 64) of tile 1 in LDS; the first half
+  // holds its rows of tile 1, the second half its rows of tile 2 in flight
+  fetch_half(0);
+  store_half(0);
+  fetch_half(1);
+  if (half == 1) {
+    store_half(1);
+    fetch_half(2);
+  }
   __syncthreads();
+  matrix_phase(std::false_type{}, -1, 0);  // S, dP of block 0
 
   if (half == 1) __syncthreads();  // the second half runs one phase behind
-  for (int it = 0; it < n_it; ++it) {
-    phase_a(it);
-    if (half == 1) {  // tile it + 1 over tile it - 1, tile it + 2 in flight
-      store(it + 1);
-      fetch(it + 2);
-    }
+  for (int j = 0; j < n_it; ++j) {
+    store_half(j + 1 + half);
+    vector_phase(j);
     __syncthreads();
-    phase_b(it);
-    if (half == 0) {
-      store(it + 1);
-      fetch(it + 2);
-    }
+    __builtin_amdgcn_s_setprio(1);
+    matrix_phase(std::true_type{}, j, j + 2 + half);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();
   }
   if (half == 0) __syncthreads();
