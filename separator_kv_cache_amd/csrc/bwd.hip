@@ -154,23 +154,35 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
 
   for (int t = 0; t < ks.n_tiles; ++t) {
     const int cur = t & 1;
-    fetch(t + 1);  // all-absent past the last tile
-    ks.issue_idx(t + 2, rows);
     const bf16* kt = kbuf(cur);
     const bf16* vt = vbuf(cur);
 
+    // S^T and dP^T as one stream of MFMAs (S, dP alternating) whose LDS
+    // operand reads run PD MFMAs ahead; the next tile's loads are issued
+    // after the first MFMAs, so their address work runs beside the matrix
+    // core instead of in front of it.
+    constexpr int NSD = 2 * NKK * NKB, PD = 4;
+    auto opnd = [&](int i) -> bf16x8 {
+      const int kk = i / (2 * NKB), x = (i >> 1) % NKB;
+      return *(const bf16x8*)(((i & 1) ? vt : kt) + (x * 32 + qn) * STR + kk * 16 + hh * 8);
+    };
     f32x16 sacc[NKB], dpacc[NKB];
 #pragma unroll
     for (int x = 0; x < NKB; ++x) { sacc[x] = f32x16{}; dpacc[x] = f32x16{}; }
+    bf16x8 op[NSD];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
+    for (int i = 0; i < PD; ++i) op[i] = opnd(i);
 #pragma unroll
-      for (int x = 0; x < NKB; ++x) {
-        const bf16x8 ka = *(const bf16x8*)(kt + (x * 32 + qn) * STR + kk * 16 + hh * 8);
-        sacc[x] = mfma32x16(ka, qreg[kk], sacc[x]);
-        const bf16x8 va = *(const bf16x8*)(vt + (x * 32 + qn) * STR + kk * 16 + hh * 8);
-        dpacc[x] = mfma32x16(va, doreg[kk], dpacc[x]);
+    for (int i = 0; i < NSD; ++i) {
+      if (i + PD < NSD) op[i + PD] = opnd(i + PD);
+      if (i == 2) {
+        fetch(t + 1);  // all-absent past the last tile
+        ks.issue_idx(t + 2, rows);
       }
+      const int kk = i / (2 * NKB), x = (i >> 1) % NKB;
+      if (i & 1) dpacc[x] = mfma32x16(op[i], doreg[kk], dpacc[x]);
+      else sacc[x] = mfma32x16(op[i], qreg[kk], sacc[x]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // dS^T = P^T (dP^T - D), kept in sacc; masked keys get P = exp2(-inf) = 0

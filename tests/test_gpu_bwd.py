@@ -86,6 +86,10 @@ EDGE = [
     (1, 8, 2, 700, 128, 2, 300, 0.12),
     (1, 2, 1, 1500, 64, 4, 1000, 0.05),
     (1, 2, 2, 129, 64, 1, 3, 0.4),
+    # 256-row query tiles (n > 256): one or two key tiles, rows past L, no sinks
+    (2, 4, 2, 260, 128, 4, 257, 0.2),
+    (1, 2, 1, 64, 128, 4, 300, 0.3),
+    (1, 4, 4, 1030, 64, 0, 600, 0.25),
 ]
 
 
