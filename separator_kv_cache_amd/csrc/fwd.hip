@@ -298,7 +298,8 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
 // shared interval both groups write their halves of K(t+2) and V(t+1) into
 // LDS (group 0 from its V phase, group 1 from its C phase), over the buffers
 // of K(t) and V(t-1), which every wave finished reading an interval earlier.
-// Each group then starts the global loads of its halves of K(t+3), V(t+2).
+// Each group starts the global loads of its halves of K(t+3), V(t+2) after
+// the first MFMAs of its C(t+1), where the issue overlaps the matrix core.
 // The separator masks of the tiles rotate through four slots: tile t's mask
 // is read in V(t-1) while K(t+2)'s is written in the same interval.
 
@@ -358,11 +359,14 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(FwdParams p) {
       if (lane == 0) *fslot(t) = bits;
     }
   };
-  // Store site of interval t: K(t+2), V(t+1) into LDS, then start K(t+3), V(t+2).
-  auto store_and_fetch = [&](int t) {
+  // Store site of interval t: K(t+2), V(t+1) into LDS; the loads of K(t+3),
+  // V(t+2) start after the first MFMAs of the next matrix phase.
+  auto store_site = [&](int t) {
     mk.template store<KSTR>(kbuf(t + 2));
     mv.template store<VSTR>(vbuf(t + 1));
     store_flag(t + 2);
+  };
+  auto fetch_site = [&](int t) {
     ks.keys(t + 3, rows, key_k);
     mk.load(krs, krow, key_k);
     mv.load(vrs, vrow, key_v);
@@ -383,7 +387,7 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(FwdParams p) {
   // (NP MFMAs) as one stream whose LDS operand reads run PD MFMAs ahead, so
   // a wave alone keeps the matrix core fed (sched_barrier pins the order).
   constexpr int NS = KK * NKB, NP = (BK / 16) * NDB, PD = 4;
-  auto matrix_phase = [&](const bf16* kt, const bf16* vt) {
+  auto matrix_phase = [&](const bf16* kt, const bf16* vt, int fetch_t) {
     const int g = lane >> 4, li = lane & 15;
     auto opnd = [&](int i) -> bf16x8 {
       if (i < NS) return *(const bf16x8*)(kt + ((i % NKB) * 32 + qn) * KSTR + (i / NKB) * 16 + hh * 8);
@@ -403,6 +407,7 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < NS + NP; ++i) {
       if (i + PD < NS + NP) op[i + PD] = opnd(i + PD);
+      if (i == 2 && fetch_t >= 0) fetch_site(fetch_t);  // beside the MFMAs, not in front of them
       if (i < NS) {
         sacc[i % NKB] = mfma32x16(op[i], qreg[i / NKB], sacc[i % NKB]);
       } else {
@@ -464,13 +469,13 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(FwdParams p) {
   for (int t = 0; t < ks.n_tiles; ++t) {
     // ---- C(t)
     __builtin_amdgcn_s_setprio(1);
-    matrix_phase(kbuf(t + 1), vbuf(t));
+    matrix_phase(kbuf(t + 1), vbuf(t), t - 1);
     __builtin_amdgcn_s_setprio(0);
-    if (grp == 1) store_and_fetch(t);
+    if (grp == 1) store_site(t);
     __syncthreads();
     // ---- V(t)
     if (t + 1 < ks.n_tiles) vector_phase(t + 1);
-    if (grp == 0) store_and_fetch(t);
+    if (grp == 0) store_site(t);
     __syncthreads();
   }
   if (grp == 0) __syncthreads();
