@@ -61,7 +61,7 @@ class PrefillLeg:
     def step(self):
         wl, e = self.wl, self.ev
         e[0].record()
-        self.mask = sa.build_mask(self.tok, synth.SEP_IDS, wl.a, wl.n)
+        sa.build_mask(self.tok, synth.SEP_IDS, wl.a, wl.n, out=self.mask)  # rebuilt in place
         e[1].record()
         sa.sepattn_fwd(self.q, self.k, self.v, self.mask, self.scale, out=self.o, lse=self.lse)
         e[2].record()

@@ -60,12 +60,19 @@ class Mask:
     def kept(self): return self._view("kept", torch.int64, (self.B,))
 
 
-def build_mask(tok: torch.Tensor, sep_ids, a: int, n: int) -> Mask:
-    """sepattn_build_mask: tok int32 [B, L] on the device."""
+def build_mask(tok: torch.Tensor, sep_ids, a: int, n: int, out: Mask | None = None) -> Mask:
+    """sepattn_build_mask: tok int32 [B, L] on the device.  With `out` (a
+    Mask of the same B, L, a, n) the metadata is rebuilt in its buffer, so a
+    loop that rebuilds masks allocates nothing."""
     if tok.dtype != torch.int32 or tok.dim() != 2 or not tok.is_contiguous():
         raise ValueError("tok must be a contiguous int32 [B, L] tensor")
     B, L = tok.shape
-    m = Mask(B, L, a, n, tok.device)
+    if out is not None:
+        if (out.B, out.L, out.a, out.n) != (B, L, a, n):
+            raise ValueError(f"out mask is B={out.B} L={out.L} a={out.a} n={out.n}, need {B} {L} {a} {n}")
+        m = out
+    else:
+        m = Mask(B, L, a, n, tok.device)
     ids = (ctypes.c_int32 * len(sep_ids))(*[int(x) for x in sep_ids])
     check(_lib.load().sepattn_build_mask(_ptr(tok), ids, len(sep_ids), ctypes.byref(m.c), _stream()))
     return m

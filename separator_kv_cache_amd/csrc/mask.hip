@@ -5,10 +5,13 @@
 // the given separator ids; query i keeps key j <= i when j < a, i - j < n or
 // token j is a separator.
 //
-// One workgroup of 1024 threads per sequence: each thread owns a contiguous
-// run of positions, counts separators and plain tokens in it, a block-wide
-// exclusive scan gives every run its output offsets, and a second pass writes
-// the compacted lists, the prefix counts and the per-row kept counts.
+// One workgroup of 1024 threads per sequence walks it in chunks of 1024
+// positions, thread x taking position c0 + x, so every load and store of a
+// wave is contiguous.  A thread first loads its tokens of up to kBatch chunks
+// (one latency for all of them); per chunk, wave ballots rank the separators
+// and plain tokens inside each wave, the waves' counts go through a
+// double-buffered table in LDS (one barrier per chunk), and a running carry
+// gives every position its offsets in the compacted lists.
 #include "common.h"
 #include "traverse.h"
 
@@ -21,33 +24,12 @@ struct SepIds {
 
 constexpr int kScanThreads = 1024;
 constexpr int kWaves = kScanThreads / 64;
+constexpr int kBatch = 16;  // chunks whose tokens a thread holds at once
 
 __device__ __forceinline__ bool is_separator(int tok, const SepIds& ids) {
   bool f = false;
   for (int k = 0; k < ids.n; ++k) f |= (tok == ids.id[k]);
   return f;
-}
-
-// Exclusive scan of two counters over the block; also returns the totals.
-__device__ void block_scan2(int x, int y, int* ex, int* ey, int* tx, int* ty) {
-  __shared__ int wx[kWaves], wy[kWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int ix = x, iy = y;
-  for (int o = 1; o < 64; o <<= 1) {
-    int ux = __shfl_up(ix, o, 64), uy = __shfl_up(iy, o, 64);
-    if (lane >= o) { ix += ux; iy += uy; }
-  }
-  if (lane == 63) { wx[wave] = ix; wy[wave] = iy; }
-  __syncthreads();
-  int bx = 0, by = 0, sx = 0, sy = 0;
-  for (int w = 0; w < kWaves; ++w) {
-    if (w < wave) { bx += wx[w]; by += wy[w]; }
-    sx += wx[w]; sy += wy[w];
-  }
-  *ex = bx + ix - x;
-  *ey = by + iy - y;
-  *tx = sx;
-  *ty = sy;
 }
 
 __device__ long long block_sum64(long long v) {
@@ -69,50 +51,77 @@ __global__ __launch_bounds__(kScanThreads) void build_mask_kernel(
     uint8_t* __restrict__ is_sep, int32_t* __restrict__ sep_idx, int32_t* __restrict__ sep_before,
     int32_t* __restrict__ sep_cnt, int32_t* __restrict__ plain_idx, int32_t* __restrict__ plain_cnt,
     int64_t* __restrict__ kept) {
+  __shared__ int cnt[2][2][kWaves];  // [chunk parity][separators, plain tokens][wave]
   const int b = blockIdx.x;
-  const int per = (L + kScanThreads - 1) / kScanThreads;
-  const int p0 = min(L, (int)threadIdx.x * per), p1 = min(L, p0 + per);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int32_t* tk = every > 0 ? nullptr : tok + (size_t)b * L;
-  auto flag = [&](int j) { return every > 0 ? (j + 1) % every == 0 : is_separator(tk[j], ids); };
-
-  int cs = 0, cp = 0;
-  for (int j = p0; j < p1; ++j) {
-    const bool f = flag(j);
-    is_sep[(size_t)b * L + j] = f ? 1 : 0;
-    if (j >= a) {
-      cs += f ? 1 : 0;
-      cp += f ? 0 : 1;
-    }
-  }
-  int os, op, ts, tp;
-  block_scan2(cs, cp, &os, &op, &ts, &tp);
-
+  uint8_t* fs = is_sep + (size_t)b * L;
   int32_t* sb = sep_before + (size_t)b * (L + 1);
   int32_t* si = sep_idx + (size_t)b * L;
   int32_t* pi = plain_idx + (size_t)b * L;
+  const uint64_t below = (1ull << lane) - 1ull;  // lanes under this one
+
+  int carry_s = 0, carry_p = 0;  // separators / plain tokens (positions >= a) before the chunk
   long long kl = 0;
-  for (int j = p0; j < p1; ++j) {
-    const bool f = flag(j);
-    sb[j] = os;
-    // kept pairs of row j: its sinks and its window positions past the
-    // sinks ...
-    kl += min(j + 1, a) + max(0, j - max(a, j - n + 1) + 1);
-    // ... plus, summed over rows, the separators left of each window:
-    // row i contributes sep_before[i - n + 1] for i >= n - 1, i.e. every
-    // position x <= L - n contributes sep_before[x] once.
-    if (j <= L - n) kl += os;
-    if (j >= a) {
-      if (f) si[os++] = j;
-      else pi[op++] = j;
+  const int n_chunks = (L + kScanThreads - 1) / kScanThreads;
+  for (int c_base = 0; c_base < n_chunks; c_base += kBatch) {
+    int tv[kBatch];
+    if (every == 0) {
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int j = (c_base + k) * kScanThreads + (int)threadIdx.x;
+        tv[k] = j < L ? tk[j] : 0;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int c = c_base + k;
+      if (c >= n_chunks) break;  // uniform
+      const int j = c * kScanThreads + (int)threadIdx.x;
+      const bool in = j < L;
+      const bool f = in && (every > 0 ? (j + 1) % every == 0 : is_separator(tv[k], ids));
+      const bool cs = f && j >= a, cp = in && !f && j >= a;
+      const uint64_t ms = __ballot(cs), mp = __ballot(cp);
+      int* t = cnt[c & 1][0];
+      if (lane == 0) {
+        t[wave] = __popcll(ms);
+        cnt[c & 1][1][wave] = __popcll(mp);
+      }
+      __syncthreads();
+      int ws = 0, wp = 0, tot_s = 0, tot_p = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int xs = cnt[c & 1][0][w], xp = cnt[c & 1][1][w];
+        if (w < wave) { ws += xs; wp += xp; }
+        tot_s += xs;
+        tot_p += xp;
+      }
+      const int os = carry_s + ws + __popcll(ms & below);  // separators (>= a) before j
+      const int op = carry_p + wp + __popcll(mp & below);
+      if (in) {
+        fs[j] = f ? 1 : 0;
+        sb[j] = os;
+        // kept pairs of row j: its sinks and its window positions past the
+        // sinks ...
+        kl += min(j + 1, a) + max(0, j - max(a, j - n + 1) + 1);
+        // ... plus, summed over rows, the separators left of each window:
+        // row i contributes sep_before[i - n + 1] for i >= n - 1, i.e. every
+        // position x <= L - n contributes sep_before[x] once.
+        if (j <= L - n) kl += os;
+        if (cs) si[os] = j;
+        if (cp) pi[op] = j;
+      }
+      carry_s += tot_s;
+      carry_p += tot_p;
     }
   }
-  for (int j = ts + threadIdx.x; j < L; j += kScanThreads) si[j] = L;
-  for (int j = tp + threadIdx.x; j < L; j += kScanThreads) pi[j] = L;
+  for (int j = carry_s + (int)threadIdx.x; j < L; j += kScanThreads) si[j] = L;
+  for (int j = carry_p + (int)threadIdx.x; j < L; j += kScanThreads) pi[j] = L;
   const long long total = block_sum64(kl);
   if (threadIdx.x == 0) {
-    sb[L] = ts;
-    sep_cnt[b] = ts;
-    plain_cnt[b] = tp;
+    sb[L] = carry_s;
+    sep_cnt[b] = carry_s;
+    plain_cnt[b] = carry_p;
     kept[b] = total;
   }
 }
