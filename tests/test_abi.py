@@ -132,3 +132,18 @@ def test_argument_validation_without_gpu():
     assert lib.sepcache_prefill(ctypes.byref(c), None, p, st3, st3, ctypes.byref(mk), None) == _lib.EINVAL
     bad = (ctypes.c_int64 * 3)(0, 0, 65)
     assert lib.sepcache_prefill(ctypes.byref(c), p, p, bad, st3, ctypes.byref(mk), None) == _lib.EINVAL
+
+
+def test_mask_rebuild_target_must_match():
+    """build_mask(out=...) rebuilds into an existing Mask only if it
+    describes the same B, L, a and n; a mismatch is refused before any
+    device call (here on CPU tensors)."""
+    import torch
+    from separator_kv_cache_amd import binding as sa
+    tok = torch.zeros((2, 40), dtype=torch.int32)
+    m = sa.Mask(2, 40, 4, 8, device="cpu")
+    for bad in (sa.Mask(1, 40, 4, 8, device="cpu"), sa.Mask(2, 41, 4, 8, device="cpu"),
+                sa.Mask(2, 40, 3, 8, device="cpu"), sa.Mask(2, 40, 4, 9, device="cpu")):
+        with pytest.raises(ValueError, match="out mask"):
+            sa.build_mask(tok, [5], 4, 8, out=bad)
+    assert (m.B, m.L, m.a, m.n) == (2, 40, 4, 8)
