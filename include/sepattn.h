@@ -188,7 +188,9 @@ SEPATTN_API int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mas
 typedef struct {
   int B, Hkv, d;       /* streams, KV heads, head dim (64 or 128)              */
   int a, s, n;         /* sinks, separator capacity (>= 0), window (>= 1)       */
-  void* k;             /* bf16 [B, Hkv, slots, d] keys before RoPE              */
+  void* k;             /* bf16 keys before RoPE: B * Hkv slices of
+                          sepcache_k_rows(slots) * d elements, each in 16-row
+                          tiles, chunk-major (see below)                       */
   void* v;             /* bf16 [B, Hkv, slots, d]                               */
   int32_t* slot_pos;   /* [B, Hkv, slots] original position held, -1 if empty  */
   uint8_t* slot_sep;   /* [B, Hkv, slots] separator flag of the token held     */
@@ -205,6 +207,13 @@ typedef struct {
 /* Physical slots per stream and KV head: max(c, a + s + n) + 1; -1 for
  * invalid sizes (a < 0, s < 0, n < 1, or 0 < c < a + s + n). */
 SEPATTN_API int sepcache_slots(int a, int s, int n, int c);
+/* Rows of one (stream, KV head) slice of k: slots rounded up to a multiple of
+ * 16.  Within the slice, the 16-byte chunk ch (dims 8 ch .. 8 ch + 7) of the
+ * key in slot r sits at chunk index ((r / 16) * (d / 8) + ch) * 16 + r % 16,
+ * so a 16-row tile is contiguous and, inside it, chunk-major: the decode
+ * reads each chunk of 16 keys with one contiguous load.  The padding rows
+ * hold zeros after sepcache_reset and are never written.  -1 for slots < 1. */
+SEPATTN_API int sepcache_k_rows(int slots);
 /* Empty every stream (slot_pos = -1, counters 0, K and V zero) of every KV
  * head. */
 SEPATTN_API int sepcache_reset(const sepcache* c, void* stream);

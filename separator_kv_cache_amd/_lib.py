@@ -46,6 +46,7 @@ _SIGS = {
                             c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                             c_void_p, c_void_p, c_size_t, c_void_p]),
     "sepcache_slots": (c_int, [c_int, c_int, c_int, c_int]),
+    "sepcache_k_rows": (c_int, [c_int]),
     "sepcache_reset": (c_int, [POINTER(SepCacheStruct), c_void_p]),
     "sepcache_append": (c_int, [POINTER(SepCacheStruct), c_void_p, c_void_p, c_void_p, c_void_p]),
     "sepcache_evict": (c_int, [POINTER(SepCacheStruct), c_void_p]),

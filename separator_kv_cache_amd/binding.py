@@ -158,7 +158,9 @@ class SepCache:
             raise ValueError(f"bad cache sizes a={a} s={s} n={n} c={cap}")
         self.B, self.Hkv, self.d, self.a, self.s, self.n, self.slots = B, Hkv, d, a, s, n, slots
         self.cap = slots - 1
-        self.k = torch.zeros((B, Hkv, slots, d), dtype=torch.bfloat16, device=device)
+        # K in the library's tiled layout: sepcache_k_rows(slots) rows per
+        # (stream, KV head), 16-row tiles stored chunk-major (sepattn.h)
+        self.k = torch.zeros((B, Hkv, lib.sepcache_k_rows(slots), d), dtype=torch.bfloat16, device=device)
         self.v = torch.zeros((B, Hkv, slots, d), dtype=torch.bfloat16, device=device)
         self.slot_pos = torch.empty((B, Hkv, slots), dtype=torch.int32, device=device)
         self.slot_sep = torch.empty((B, Hkv, slots), dtype=torch.uint8, device=device)

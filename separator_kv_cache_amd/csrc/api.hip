@@ -214,6 +214,8 @@ int sepcache_slots(int a, int s, int n, int c) {
   return cap + 1 > 65536 ? -1 : (int)(cap + 1);
 }
 
+int sepcache_k_rows(int slots) { return slots < 1 || slots > 65536 ? -1 : sepcache_k_rows_of(slots); }
+
 static int check_cache(const sepcache* c, const char* who) {
   if (!c) return sepattn_fail(SEPATTN_EINVAL, "%s: null cache", who);
   if (c->B <= 0 || c->Hkv <= 0) return sepattn_fail(SEPATTN_EINVAL, "%s: B=%d Hkv=%d", who, c->B, c->Hkv);

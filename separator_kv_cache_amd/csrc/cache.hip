@@ -36,6 +36,15 @@ struct CacheParams {
   int B, Hkv, d, a, s, n, slots, P;
 };
 
+// K of one (stream, KV head) is stored per 16-row tile, chunk-major: 16-byte
+// chunk ch of row r sits at chunk index ((r / 16) * nch + ch) * 16 + r % 16
+// of the slice, which has sepcache_k_rows_of(slots) rows.  The decode's
+// score operand of a 16-row tile (lane (g, col) holds chunk 4m + g of row
+// 16t + col) is then 1 KB contiguous per load.  V is row-major.
+__device__ __forceinline__ size_t k_at(int row, int ch, int nch) {  // element offset of chunk ch of row
+  return ((((size_t)(row >> 4) * nch + ch) << 4) + (size_t)(row & 15)) * 8;
+}
+
 int past_entries(const sepcache* c) { return c->c > c->a + c->s + c->n ? c->c - (c->a + c->s + c->n) : 0; }
 
 CacheParams make_params(const sepcache* c) {
@@ -166,12 +175,12 @@ __global__ void reset_kernel(CacheParams p) {
   }
   // K and V of every slot to zero: decode multiplies the rows that hold no
   // entry by a zero probability, which must not meet a non-finite value
-  const size_t chunks = (size_t)p.slots * p.d / 8;
+  // (K's slice includes the padding rows of its last tile)
+  const size_t kchunks = (size_t)sepcache_k_rows_of(p.slots) * p.d / 8, vchunks = (size_t)p.slots * p.d / 8;
   const u32x4 z = {0u, 0u, 0u, 0u};
-  for (size_t i = threadIdx.x; i < chunks; i += blockDim.x) {
-    st16(p.k + bh * p.slots * p.d + i * 8, z);
-    st16(p.v + bh * p.slots * p.d + i * 8, z);
-  }
+  bf16* kz = p.k + bh * sepcache_k_rows_of(p.slots) * p.d;
+  for (size_t i = threadIdx.x; i < kchunks; i += blockDim.x) st16(kz + i * 8, z);
+  for (size_t i = threadIdx.x; i < vchunks; i += blockDim.x) st16(p.v + bh * p.slots * p.d + i * 8, z);
   if (threadIdx.x < 8) p.state[bh * 8 + threadIdx.x] = 0;
 }
 
@@ -202,7 +211,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(CacheParams p, cons
   const bf16* vp = v + b * vsb + h * vsh;
   int32_t* spos = p.slot_pos + (size_t)bh * p.slots;
   uint8_t* ssep = p.slot_sep + (size_t)bh * p.slots;
-  bf16* kc = p.k + (size_t)bh * p.slots * p.d;
+  bf16* kc = p.k + (size_t)bh * sepcache_k_rows_of(p.slots) * p.d;
   bf16* vc = p.v + (size_t)bh * p.slots * p.d;
   auto token_of = [&](int slot) -> int {
     if (slot < p.a) return slot < L ? slot : -1;
@@ -244,7 +253,7 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(CacheParams p, cons
   for (int u = 0; u < PF_PER_THREAD; ++u) {
     const int i = i0 + u * PF_THREADS;
     if (i < p.slots * NCH) {
-      st16(kc + (size_t)(i / NCH) * p.d + (i % NCH) * 8, kx[u]);
+      st16(kc + k_at(i / NCH, i % NCH, NCH), kx[u]);
       st16(vc + (size_t)(i / NCH) * p.d + (i % NCH) * 8, vx[u]);
     }
   }
@@ -268,11 +277,22 @@ __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(CacheParams p, cons
   }
 }
 
-// Copies one row (d elements of K and of V) with the workgroup's threads.
-__device__ __forceinline__ void copy_row(int d, const bf16* ks, const bf16* vs, bf16* kd, bf16* vd) {
+// Stores a new row (d elements of K and of V, contiguous) into slot `dst`
+// with the workgroup's threads: K into the tiled slice, V row-major.
+__device__ __forceinline__ void store_row(int d, const bf16* ks, const bf16* vs, bf16* kslice, int dst, bf16* vd) {
   const int ch = d / 8;
   for (int i = threadIdx.x; i < 2 * ch; i += blockDim.x) {
-    if (i < ch) st16(kd + i * 8, ld16(ks + i * 8));
+    if (i < ch) st16(kslice + k_at(dst, i, ch), ld16(ks + i * 8));
+    else st16(vd + (i - ch) * 8, ld16(vs + (i - ch) * 8));
+  }
+}
+
+// Moves the row of slot `src` to slot `dst` (K in the tiled slice, V
+// row-major) with the workgroup's threads.
+__device__ __forceinline__ void move_row(int d, bf16* kslice, int src, int dst, const bf16* vs, bf16* vd) {
+  const int ch = d / 8;
+  for (int i = threadIdx.x; i < 2 * ch; i += blockDim.x) {
+    if (i < ch) st16(kslice + k_at(dst, i, ch), ld16(kslice + k_at(src, i, ch)));
     else st16(vd + (i - ch) * 8, ld16(vs + (i - ch) * 8));
   }
 }
@@ -290,14 +310,11 @@ __global__ __launch_bounds__(64) void update_kernel(CacheParams p, const bf16* k
   const Transition tr = transition(c0, p.a, p.s, p.n, do_append, new_sep, do_evict);
   const int ev_pos = tr.evicted ? spos[tr.ev_src] : -1;
   const int new_oldsep = tr.refresh_oldsep ? ssep[p.a + p.s + tr.after.winh] : 0;
-  bf16* kb = p.k + (size_t)bh * p.slots * p.d;
+  bf16* kb = p.k + (size_t)bh * sepcache_k_rows_of(p.slots) * p.d;
   bf16* vb = p.v + (size_t)bh * p.slots * p.d;
   if (tr.app_slot >= 0)
-    copy_row(p.d, k_new + (size_t)bh * p.d, v_new + (size_t)bh * p.d, kb + (size_t)tr.app_slot * p.d,
-             vb + (size_t)tr.app_slot * p.d);
-  if (tr.ev_dst >= 0)
-    copy_row(p.d, kb + (size_t)tr.ev_src * p.d, vb + (size_t)tr.ev_src * p.d, kb + (size_t)tr.ev_dst * p.d,
-             vb + (size_t)tr.ev_dst * p.d);
+    store_row(p.d, k_new + (size_t)bh * p.d, v_new + (size_t)bh * p.d, kb, tr.app_slot, vb + (size_t)tr.app_slot * p.d);
+  if (tr.ev_dst >= 0) move_row(p.d, kb, tr.ev_src, tr.ev_dst, vb + (size_t)tr.ev_src * p.d, vb + (size_t)tr.ev_dst * p.d);
   __syncthreads();
   if (threadIdx.x == 0) commit(tr, st, spos, ssep, new_sep, ev_pos, new_oldsep);
 }
@@ -312,7 +329,7 @@ __global__ __launch_bounds__(64) void flush_kernel(CacheParams p) {
   int32_t* st = p.state + (size_t)bh * 8;
   int32_t* spos = p.slot_pos + (size_t)bh * p.slots;
   uint8_t* ssep = p.slot_sep + (size_t)bh * p.slots;
-  bf16* kb = p.k + (size_t)bh * p.slots * p.d;
+  bf16* kb = p.k + (size_t)bh * sepcache_k_rows_of(p.slots) * p.d;
   bf16* vb = p.v + (size_t)bh * p.slots * p.d;
   const Counters c = load_counters(st);
   if (c.winc < p.n) return;  // p.n = n + P, the queue's capacity
@@ -338,7 +355,7 @@ __global__ __launch_bounds__(64) void flush_kernel(CacheParams p) {
     if (sep && p.s > 0 && i >= keep_from) {
       const int dst = p.a + (c.seph + c.sepc + i) % p.s;
       for (int ch = 0; ch < p.d / 8; ++ch) {
-        st16(kb + (size_t)dst * p.d + ch * 8, ld16(kb + (size_t)src * p.d + ch * 8));
+        st16(kb + k_at(dst, ch, p.d / 8), ld16(kb + k_at(src, ch, p.d / 8)));
         st16(vb + (size_t)dst * p.d + ch * 8, ld16(vb + (size_t)src * p.d + ch * 8));
       }
       spos[dst] = spos[src];
@@ -482,7 +499,7 @@ __global__ __launch_bounds__(SPLIT_THREADS) void attend_part(AttendParams p) {
   const int b = bh / c.Hkv, kvh = bh % c.Hkv;
   const int li = threadIdx.x % LPR, grp = threadIdx.x / LPR;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  bf16* kb = c.k + (size_t)bh * c.slots * D;
+  bf16* kb = c.k + (size_t)bh * sepcache_k_rows_of(c.slots) * D;
   bf16* vb = c.v + (size_t)bh * c.slots * D;
   const int rows = c.slots + (UPDATE ? 1 : 0);
   const int per = (rows + p.split - 1) / p.split;
@@ -500,10 +517,11 @@ __global__ __launch_bounds__(SPLIT_THREADS) void attend_part(AttendParams p) {
   for (int r = 0; r < MAXR; ++r) {
     const int row = min(row0 + grp + r * GROUPS, rows - 1);
     const bool cached = row < c.slots;
-    const bf16* ks = cached ? kb + (size_t)row * D : p.k_new + (size_t)bh * D;
+    const bf16* kn = p.k_new + (size_t)bh * D;
     const bf16* vs = cached ? vb + (size_t)row * D : p.v_new + (size_t)bh * D;
-    klo[r] = *(const bf16x4*)(ks + li * 4);
-    khi[r] = *(const bf16x4*)(ks + HALF + li * 4);
+    // dims li * 4 .. + 3 and HALF + li * 4 .. + 3 (each inside one 16-byte chunk)
+    klo[r] = *(const bf16x4*)(cached ? kb + k_at(row, li / 2, D / 8) + (li & 1) * 4 : kn + li * 4);
+    khi[r] = *(const bf16x4*)(cached ? kb + k_at(row, (HALF + li * 4) / 8, D / 8) + (li & 1) * 4 : kn + HALF + li * 4);
     vlo[r] = *(const bf16x4*)(vs + li * 4);
     vhi[r] = *(const bf16x4*)(vs + HALF + li * 4);
   }
@@ -684,10 +702,9 @@ __global__ __launch_bounds__(SPLIT_THREADS) void attend_part(AttendParams p) {
         else if (row == tr.ev_src) dst = tr.ev_dst;
       }
       if (dst >= 0) {
-        bf16* kd = kb + (size_t)dst * D;
         bf16* vd = vb + (size_t)dst * D;
-        *(bf16x4*)(kd + li * 4) = klo[r];
-        *(bf16x4*)(kd + HALF + li * 4) = khi[r];
+        *(bf16x4*)(kb + k_at(dst, li / 2, D / 8) + (li & 1) * 4) = klo[r];
+        *(bf16x4*)(kb + k_at(dst, (HALF + li * 4) / 8, D / 8) + (li & 1) * 4) = khi[r];
         *(bf16x4*)(vd + li * 4) = vlo[r];
         *(bf16x4*)(vd + HALF + li * 4) = vhi[r];
       }
@@ -921,7 +938,7 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(const int32_t* state,
   const int tps = (n_tiles + nsplit - 1) / nsplit;
   const int t_lo = split * tps, t_hi = min(t_lo + tps, n_tiles);  // this workgroup's tiles
   const uint32_t row_bytes = D * 2;
-  bf16* kb = kc + (size_t)bh * slots * D;
+  bf16* kb = kc + (size_t)bh * sepcache_k_rows_of(slots) * D;
   bf16* vb = vc + (size_t)bh * slots * D;
   const bool lead = wave == 0;
 
@@ -973,7 +990,7 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(const int32_t* state,
   };
   const bool holds_new = UPDATE && wave == 1 && t_hi == n_tiles;
   u32x4 nk, nv;
-  const rsrc_t krs = make_rsrc(kb, (uint32_t)slots * row_bytes);
+  const rsrc_t krs = make_rsrc(kb, (uint32_t)sepcache_k_rows_of(slots) * row_bytes);
   const rsrc_t vrs = make_rsrc(vb, (uint32_t)slots * row_bytes);
   const rsrc_t prs = make_rsrc(c.slot_pos + (size_t)bh * slots, (uint32_t)slots * 4);
   u32x4 kr[DT_MAXT][NM], vr[DT_MAXT][4];
@@ -987,7 +1004,9 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(const int32_t* state,
     const uint32_t absent = (uint32_t)(t >> 31) & BUF_OOB;
     const int krow = t * DT_ROWS + col;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) kr[j][m] = bld16(krs, ((uint32_t)krow * row_bytes + (4 * m + g) * 16) | absent);
+    for (int m = 0; m < NM; ++m)  // tile-major K: 1 KB contiguous per load; rows past the slots read as zeros
+      kr[j][m] = bld16(krs, ((uint32_t)(t * DT_ROWS) * row_bytes + (uint32_t)(((4 * m + g) << 4) + col) * 16) |
+                                absent | (((uint32_t)(slots - 1 - krow) >> 31) << 31));
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       vr[j][u] = bld16(vrs, col < NCH ? ((uint32_t)(t * DT_ROWS + 4 * g + u) * row_bytes + col * 16) | absent : BUF_OOB);
@@ -1122,7 +1141,7 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(const int32_t* state,
         if (dst >= 0 && src >= row0 && src < row0 + DT_ROWS) {
           if (krow == src)
 #pragma unroll
-            for (int m = 0; m < NM; ++m) st16(kb + (size_t)dst * D + (4 * m + g) * 8, kr[j][m]);
+            for (int m = 0; m < NM; ++m) st16(kb + k_at(dst, 4 * m + g, NCH), kr[j][m]);
 #pragma unroll
           for (int u = 0; u < 4; ++u)
             if (row0 + 4 * g + u == src && col < NCH) st16(vb + (size_t)dst * D + col * 8, vr[j][u]);

@@ -58,6 +58,10 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p) {
 
 __device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
 
+// Rows of one (stream, KV head) slice of a SepCache's K: its slots rounded
+// up to whole 16-row tiles (the tiled K layout of the cache kernels).
+__host__ __device__ inline int sepcache_k_rows_of(int slots) { return (slots + 15) & ~15; }
+
 // 16-byte global loads and stores.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *(u32x4*)p = v; }

@@ -147,3 +147,25 @@ def test_mask_rebuild_target_must_match():
         with pytest.raises(ValueError, match="out mask"):
             sa.build_mask(tok, [5], 4, 8, out=bad)
     assert (m.B, m.L, m.a, m.n) == (2, 40, 4, 8)
+
+
+def test_tiled_key_layout():
+    """sepcache_k_rows pads a slice to whole 16-row tiles, and the header's
+    chunk formula (what tests.util.cache_k_rows reads back) is a bijection
+    from (slot, dim) onto the padded slice."""
+    import torch
+    from tests.util import cache_k_rows
+    lib = _lib.load()
+    assert [lib.sepcache_k_rows(x) for x in (1, 15, 16, 17, 325, 65536)] == [16, 16, 16, 32, 336, 65536]
+    assert lib.sepcache_k_rows(0) == -1 and lib.sepcache_k_rows(65537) == -1
+    for slots, d in ((325, 128), (37, 64)):
+        R, nch = lib.sepcache_k_rows(slots), d // 8
+        flat = torch.full((R * d,), -1, dtype=torch.int64)
+        for r in range(slots):
+            for e in range(d):
+                ch = e // 8
+                idx = (((r // 16) * nch + ch) * 16 + r % 16) * 8 + e % 8
+                assert flat[idx] == -1
+                flat[idx] = r * d + e
+        rows = cache_k_rows(flat.view(1, 1, R, d), slots)[0, 0]
+        assert torch.equal(rows, torch.arange(slots * d).view(slots, d))

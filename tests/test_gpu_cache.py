@@ -8,7 +8,7 @@ import torch
 from oracle import sepllm_oracle as orc
 from separator_kv_cache_amd import binding as sa
 from separator_kv_cache_amd import synth
-from tests.util import TOL_BF16, as_f64, max_abs, say
+from tests.util import TOL_BF16, as_f64, cache_k_rows, max_abs, say
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +30,7 @@ def _check_state(cache, sims, kb, vb, t):
     pos, ln = pos.cpu().numpy(), ln.cpu().numpy()
     spos = cache.slot_pos.cpu().numpy()          # [B, Hkv, slots]
     state = cache.state.cpu().numpy()
-    kc, vc = cache.k.cpu(), cache.v.cpu()
+    kc, vc = cache_k_rows(cache.k.cpu(), cache.slots), cache.v.cpu()
     for b, sim in enumerate(sims):
         order = sim.order()
         assert ln[b] == len(order), (t, b)

@@ -58,3 +58,12 @@ def max_abs(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def cache_k_rows(k, slots):
+    """The keys of a SepCache K buffer as rows [B, Hkv, slots, d], from the
+    tiled layout the C header documents (sepcache_k_rows): 16-byte chunk ch of
+    slot r at chunk index ((r / 16) * (d / 8) + ch) * 16 + r % 16."""
+    B, H, R, d = k.shape
+    t = k.reshape(B, H, R // 16, d // 8, 16, 8)  # [tile, chunk, row in tile, 8]
+    return t.permute(0, 1, 2, 4, 3, 5).reshape(B, H, R, d)[:, :, :slots]
