@@ -60,6 +60,9 @@ SMALL = [
     (1, 4, 2, 64, 2, 700, 400, 400, 0.5, False, "push"),   # 1103 slots: the split-and-merge kernels
     (1, 32, 8, 128, 4, 64, 256, 400, 0.12, True, "push"),
     (1, 32, 8, 128, 4, 64, 256, 400, 0.12, True, "step"),
+    # slots a multiple of 16: K has no padding rows, the appended row opens a tile
+    (2, 8, 2, 128, 4, 11, 16, 90, 0.4, True, "step"),      # 32 slots
+    (2, 4, 2, 64, 2, 13, 16, 90, 0.3, False, "split"),     # 32 slots
     # with a capacity c > a + s + n (a past window of c - a - s - n entries);
     # the last field is c
     (3, 4, 2, 64, 2, 3, 5, 90, 0.4, True, "step", 16),
@@ -69,6 +72,7 @@ SMALL = [
     (2, 8, 1, 128, 1, 2, 1, 60, 0.6, False, "step", 9),    # n = 1
     (2, 8, 2, 128, 4, 64, 256, 1300, 0.12, True, "step", 800),  # c = 800: 801 slots, two workgroups
     (1, 4, 2, 64, 2, 300, 400, 900, 0.5, False, "push", 1100),  # 1101 slots: the split-and-merge kernels
+    (2, 8, 2, 128, 2, 5, 9, 90, 0.5, True, "step", 47),    # 48 slots: no K padding, with a past window
 ]
 
 
