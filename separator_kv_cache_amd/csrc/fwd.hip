@@ -298,8 +298,10 @@ __global__ __launch_bounds__(WAVES * 64) void fwd_kernel(FwdParams p) {
 // shared interval both groups write their halves of K(t+2) and V(t+1) into
 // LDS (group 0 from its V phase, group 1 from its C phase), over the buffers
 // of K(t) and V(t-1), which every wave finished reading an interval earlier.
-// Each group starts the global loads of its halves of K(t+3), V(t+2) after
-// the first MFMAs of its C(t+1), where the issue overlaps the matrix core.
+// Group 0 starts the global loads of its halves of K(t+3), V(t+2) after the
+// first MFMAs of its C(t+1), where the issue overlaps the matrix core; group
+// 1, whose C phase also holds its LDS stores, starts them in its V(t), an
+// interval earlier (phase timers: its C phase bounded the shared interval).
 // The separator masks of the tiles rotate through four slots: tile t's mask
 // is read in V(t-1) while K(t+2)'s is written in the same interval.
 
@@ -469,13 +471,14 @@ __global__ __launch_bounds__(512) void fwd_pp_kernel(FwdParams p) {
   for (int t = 0; t < ks.n_tiles; ++t) {
     // ---- C(t)
     __builtin_amdgcn_s_setprio(1);
-    matrix_phase(kbuf(t + 1), vbuf(t), t - 1);
+    matrix_phase(kbuf(t + 1), vbuf(t), grp == 0 ? t - 1 : -1);
     __builtin_amdgcn_s_setprio(0);
     if (grp == 1) store_site(t);
     __syncthreads();
     // ---- V(t)
     if (t + 1 < ks.n_tiles) vector_phase(t + 1);
     if (grp == 0) store_site(t);
+    else fetch_site(t);
     __syncthreads();
   }
   if (grp == 0) __syncthreads();
