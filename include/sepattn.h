@@ -212,7 +212,8 @@ SEPATTN_API int sepcache_slots(int a, int s, int n, int c);
  * key in slot r sits at chunk index ((r / 16) * (d / 8) + ch) * 16 + r % 16,
  * so a 16-row tile is contiguous and, inside it, chunk-major: the decode
  * reads each chunk of 16 keys with one contiguous load.  The padding rows
- * hold zeros after sepcache_reset and are never written.  -1 for slots < 1. */
+ * are neither read nor written by any call (sepcache_reset zeroes them).
+ * -1 for slots < 1 or slots > 65536. */
 SEPATTN_API int sepcache_k_rows(int slots);
 /* Empty every stream (slot_pos = -1, counters 0, K and V zero) of every KV
  * head. */
