@@ -993,6 +993,9 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(const int32_t* state,
   const rsrc_t krs = make_rsrc(kb, (uint32_t)sepcache_k_rows_of(slots) * row_bytes);
   const rsrc_t vrs = make_rsrc(vb, (uint32_t)slots * row_bytes);
   const rsrc_t prs = make_rsrc(c.slot_pos + (size_t)bh * slots, (uint32_t)slots * 4);
+  // (the tile rows are read once per step, with the non-temporal hint: the
+  // other layers' caches pass through the caches before this one is read
+  // again; measured 9.04 -> 8.78 us per layer-token on the Llama step)
   u32x4 kr[DT_MAXT][NM], vr[DT_MAXT][4];
   int spos[DT_MAXT];
   // An absent tile (t = -1) sets the offsets' top bit arithmetically rather
@@ -1005,11 +1008,11 @@ __global__ __launch_bounds__(DT_THREADS) void decode_tiles(const int32_t* state,
     const int krow = t * DT_ROWS + col;
 #pragma unroll
     for (int m = 0; m < NM; ++m)  // tile-major K: 1 KB contiguous per load; rows past the slots read as zeros
-      kr[j][m] = bld16(krs, ((uint32_t)(t * DT_ROWS) * row_bytes + (uint32_t)(((4 * m + g) << 4) + col) * 16) |
-                                absent | (((uint32_t)(slots - 1 - krow) >> 31) << 31));
+      kr[j][m] = bld16_nt(krs, ((uint32_t)(t * DT_ROWS) * row_bytes + (uint32_t)(((4 * m + g) << 4) + col) * 16) |
+                                   absent | (((uint32_t)(slots - 1 - krow) >> 31) << 31));
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      vr[j][u] = bld16(vrs, col < NCH ? ((uint32_t)(t * DT_ROWS + 4 * g + u) * row_bytes + col * 16) | absent : BUF_OOB);
+      vr[j][u] = bld16_nt(vrs, col < NCH ? ((uint32_t)(t * DT_ROWS + 4 * g + u) * row_bytes + col * 16) | absent : BUF_OOB);
     if constexpr (!SHIFT) spos[j] = bld4(prs, ((uint32_t)krow * 4) | absent);
     // after the first tile's loads: its pointers come from the struct
     if (j == 0 && holds_new) {

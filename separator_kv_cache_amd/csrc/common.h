@@ -78,6 +78,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 bld16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
+// The same with the non-temporal hint (nt): for rows a launch reads once
+// and that other launches' data will displace before they are read again.
+__device__ __forceinline__ u32x4 bld16_nt(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
 __device__ __forceinline__ int bld4(rsrc_t r, uint32_t off) {
   return (int)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
