@@ -265,7 +265,7 @@ size_t sepcache_decode_workspace_size(const sepcache* c, int Hq) {
   return sepcache_decode_ws_bytes(c, Hq);
 }
 
-static int check_attend(const sepcache* c, int Hq, const void* q, float scale, int shift, void* o, const char* who) {
+static int check_attend(const sepcache* c, int Hq, const void* q, float scale, void* o, const char* who) {
   SEPATTN_TRY(check_cache(c, who));
   if (Hq <= 0 || Hq % c->Hkv != 0)
     return sepattn_fail(SEPATTN_EINVAL, "%s: Hq=%d is not a positive multiple of Hkv=%d", who, Hq, c->Hkv);
@@ -289,7 +289,7 @@ static int check_ws(const sepcache* c, int Hq, const void* ws, size_t bytes, con
 int sepcache_decode(const sepcache* c, int Hq, const void* q, float scale, int shift, void* o, void* workspace,
                     size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
-  SEPATTN_TRY(check_attend(c, Hq, q, scale, shift, o, "decode"));
+  SEPATTN_TRY(check_attend(c, Hq, q, scale, o, "decode"));
   SEPATTN_TRY(check_ws(c, Hq, workspace, workspace_bytes, "decode"));
   SEPATTN_TRY(sepattn_check_device());
   return sepcache_launch_decode(c, Hq, q, scale, shift, o, workspace, (hipStream_t)stream);
@@ -299,7 +299,7 @@ int sepcache_step(const sepcache* c, const void* k_new, const void* v_new, const
                   const void* q, float scale, int shift, void* o, void* workspace, size_t workspace_bytes,
                   void* stream) {
   g_err[0] = 0;
-  SEPATTN_TRY(check_attend(c, Hq, q, scale, shift, o, "step"));
+  SEPATTN_TRY(check_attend(c, Hq, q, scale, o, "step"));
   if (!k_new || !v_new || !is_sep) return sepattn_fail(SEPATTN_EINVAL, "step: null input");
   if (!aligned16(k_new) || !aligned16(v_new)) return sepattn_fail(SEPATTN_EINVAL, "step: K/V rows not 16-byte aligned");
   SEPATTN_TRY(check_ws(c, Hq, workspace, workspace_bytes, "step"));

@@ -832,6 +832,7 @@ constexpr int DT_MAXT = 2;    // tiles per wave
 constexpr int DT_TPW = DT_WAVES * DT_MAXT;  // tiles per workgroup
 constexpr int DT_MAX_SPLIT = 2;
 constexpr int DT_MAX_ROWS = DT_MAX_SPLIT * DT_TPW * DT_ROWS;
+static_assert(DT_MAX_ROWS == 1024, "the tiled decode covers caches of up to 1024 rows");
 constexpr int DT_NCLS = 7;    // intervals of constant rank offset
 constexpr size_t DT_TICKET_BYTES = 256;            // per 64 (stream, KV head) pairs
 

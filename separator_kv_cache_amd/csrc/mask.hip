@@ -73,7 +73,6 @@ __global__ __launch_bounds__(kScanThreads) void build_mask_kernel(
         tv[k] = j < L ? tk[j] : 0;
       }
     }
-#pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       const int c = c_base + k;
       if (c >= n_chunks) break;  // uniform
