@@ -22,7 +22,15 @@ def _stream() -> ctypes.c_void_p:
 
 
 def _ptr(t: torch.Tensor | None) -> ctypes.c_void_p:
+    if t is not None and not t.is_cuda:
+        # the kernels dereference every pointer on the device
+        raise ValueError(f"expected a device tensor, got one on {t.device}")
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _check_lse(lse: torch.Tensor, B: int, Hq: int, L: int):
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, L) or not lse.is_contiguous():
+        raise ValueError(f"lse must be contiguous fp32 [{B}, {Hq}, {L}]")
 
 
 class Mask:
@@ -35,8 +43,16 @@ class Mask:
             raise ValueError(f"bad mask size B={B} L={L}")
         self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.c = SepattnMask()
-        check(lib.sepattn_mask_carve(ctypes.byref(self.c), B, L, a, n, _ptr(self.buffer), nbytes))
+        # carving only computes the fields' addresses inside the buffer
+        check(lib.sepattn_mask_carve(ctypes.byref(self.c), B, L, a, n, ctypes.c_void_p(self.buffer.data_ptr()),
+                                     nbytes))
         self.B, self.L, self.a, self.n = B, L, a, n
+
+    def ref(self):
+        """The struct for a call that runs on the device."""
+        if not self.buffer.is_cuda:
+            raise ValueError(f"mask metadata must be in device memory, not on {self.buffer.device}")
+        return ctypes.byref(self.c)
 
     def _view(self, field: str, dtype, shape):
         off = getattr(self.c, field) - self.buffer.data_ptr()
@@ -74,7 +90,7 @@ def build_mask(tok: torch.Tensor, sep_ids, a: int, n: int, out: Mask | None = No
     else:
         m = Mask(B, L, a, n, tok.device)
     ids = (ctypes.c_int32 * len(sep_ids))(*[int(x) for x in sep_ids])
-    check(_lib.load().sepattn_build_mask(_ptr(tok), ids, len(sep_ids), ctypes.byref(m.c), _stream()))
+    check(_lib.load().sepattn_build_mask(_ptr(tok), ids, len(sep_ids), m.ref(), _stream()))
     return m
 
 
@@ -82,7 +98,7 @@ def build_mask_fixed(B: int, L: int, delta: int, a: int, n: int, device="cuda") 
     """sepattn_build_mask_fixed: fixed-interval anchors, token j kept outside
     the window iff (j + 1) % delta == 0."""
     m = Mask(B, L, a, n, device)
-    check(_lib.load().sepattn_build_mask_fixed(int(delta), ctypes.byref(m.c), _stream()))
+    check(_lib.load().sepattn_build_mask_fixed(int(delta), m.ref(), _stream()))
     return m
 
 
@@ -91,7 +107,7 @@ def mask_bits(m: Mask) -> torch.Tensor:
     (int32 storage holding the same bits)."""
     words = (m.L + 31) // 32
     bits = torch.empty((m.B, m.L, words), dtype=torch.int32, device=m.buffer.device)
-    check(_lib.load().sepattn_mask_bits(ctypes.byref(m.c), _ptr(bits), _stream()))
+    check(_lib.load().sepattn_mask_bits(m.ref(), _ptr(bits), _stream()))
     return bits
 
 
@@ -116,22 +132,29 @@ def sepattn_fwd(q, k, v, m: Mask, scale: float | None = None, out: torch.Tensor 
     """sepattn_fwd: returns (O, LSE) with O like q and LSE fp32 [B, Hq, L]."""
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share dtype bf16 or fp32")
+    if out is not None and out.dtype != q.dtype:
+        raise ValueError("out must have q's dtype")
     o = torch.empty_like(q) if out is None else out
     B, Hq, L, d = q.shape
     if want_lse and lse is None:
         lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if want_lse:
+        _check_lse(lse, B, Hq, L)
     s = _shape(q, k, v, o)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    check(_lib.load().sepattn_fwd(ctypes.byref(s), _DT[q.dtype], ctypes.byref(m.c), _ptr(q), _ptr(k), _ptr(v),
+    check(_lib.load().sepattn_fwd(ctypes.byref(s), _DT[q.dtype], m.ref(), _ptr(q), _ptr(k), _ptr(v),
                                   sc, _ptr(o), _ptr(lse if want_lse else None), _stream()))
     return o, lse
 
 
 def sepattn_bwd(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, workspace=None):
     """sepattn_bwd: returns (dQ, dK, dV)."""
-    if dout.stride() != o.stride():
-        raise ValueError("dout must have o's strides")
+    if dout.shape != o.shape or dout.stride() != o.stride():
+        raise ValueError("dout must have o's shape and strides")
+    if o.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("o and dout must have q's dtype")
     s = _shape(q, k, v, o)
+    _check_lse(lse, s.B, s.Hq, s.L)
     lib = _lib.load()
     need = lib.sepattn_bwd_workspace_size(ctypes.byref(s))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -140,7 +163,7 @@ def sepattn_bwd(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, work
     dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
     dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
     sc = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
-    check(lib.sepattn_bwd(ctypes.byref(s), _DT[q.dtype], ctypes.byref(m.c), _ptr(q), _ptr(k), _ptr(v),
+    check(lib.sepattn_bwd(ctypes.byref(s), _DT[q.dtype], m.ref(), _ptr(q), _ptr(k), _ptr(v),
                           _ptr(o), _ptr(lse), _ptr(dout), sc, _ptr(dq), _ptr(dk), _ptr(dv),
                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
     return dq, dk, dv
@@ -152,6 +175,8 @@ class SepCache:
 
     def __init__(self, B: int, Hkv: int, d: int, a: int, s: int, n: int, theta: float = 500000.0,
                  cap: int = 0, device="cuda"):
+        if torch.device(device).type != "cuda":
+            raise ValueError("a SepCache lives in device memory")
         lib = _lib.load()
         slots = lib.sepcache_slots(a, s, n, cap)
         if slots < 0:
@@ -227,6 +252,8 @@ class SepCache:
         if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[0] != self.B or q.shape[2] != self.d \
                 or not q.is_contiguous():
             raise ValueError("q must be contiguous bf16 [B, Hq, d]")
+        if out is not None and (out.dtype != q.dtype or out.shape != q.shape or not out.is_contiguous()):
+            raise ValueError("out must be a contiguous tensor like q")
         return torch.empty_like(q) if out is None else out
 
     def prefill(self, k, v, m: Mask):
@@ -238,7 +265,7 @@ class SepCache:
                 raise ValueError("k/v must be bf16 [B, Hkv, L, d] with a contiguous last dimension")
         ks = (ctypes.c_int64 * 3)(*k.stride()[:3])
         vs = (ctypes.c_int64 * 3)(*v.stride()[:3])
-        check(_lib.load().sepcache_prefill(ctypes.byref(self.c), _ptr(k), _ptr(v), ks, vs, ctypes.byref(m.c),
+        check(_lib.load().sepcache_prefill(ctypes.byref(self.c), _ptr(k), _ptr(v), ks, vs, m.ref(),
                                            _stream()))
 
     def export_order(self):

@@ -169,3 +169,35 @@ def test_tiled_key_layout():
                 flat[idx] = r * d + e
         rows = cache_k_rows(flat.view(1, 1, R, d), slots)[0, 0]
         assert torch.equal(rows, torch.arange(slots * d).view(slots, d))
+
+
+def test_binding_refuses_host_memory_and_bad_outputs():
+    """The binding hands the kernels device pointers only: host tensors, a
+    host-memory mask or cache, and outputs, log-sum-exps or output gradients
+    that do not match what the entry points assume are refused before any
+    call (here on CPU tensors, so nothing reaches a kernel)."""
+    import torch
+    from separator_kv_cache_amd import binding as sa
+    with pytest.raises(ValueError, match="device tensor"):
+        sa._ptr(torch.zeros(4))
+    assert sa._ptr(None).value is None
+    tok = torch.zeros((1, 32), dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensor"):
+        sa.build_mask(tok, [5], 4, 8)
+    m = sa.Mask(1, 32, 4, 8, device="cpu")
+    with pytest.raises(ValueError, match="device memory"):
+        m.ref()
+    with pytest.raises(ValueError, match="device memory"):
+        sa.SepCache(1, 1, 64, 4, 8, 16, device="cpu")
+    q = torch.zeros((1, 2, 32, 64), dtype=torch.bfloat16)
+    kv = torch.zeros((1, 1, 32, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="q's dtype"):
+        sa.sepattn_fwd(q, kv, kv, m, out=torch.zeros(q.shape, dtype=torch.float32))
+    with pytest.raises(ValueError, match="lse must be"):
+        sa.sepattn_fwd(q, kv, kv, m, lse=torch.zeros((1, 2, 31)))
+    with pytest.raises(ValueError, match="lse must be"):
+        sa.sepattn_bwd(q, kv, kv, q, torch.zeros((1, 2, 32), dtype=torch.float64), q, m)
+    with pytest.raises(ValueError, match="o's shape"):
+        sa.sepattn_bwd(q, kv, kv, q, torch.zeros((1, 2, 32)), q[:, :1], m)
+    with pytest.raises(ValueError, match="q's dtype"):
+        sa.sepattn_bwd(q, kv, kv, q, torch.zeros((1, 2, 32)), q.float(), m)
