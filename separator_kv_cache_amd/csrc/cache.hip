@@ -193,7 +193,10 @@ __global__ void reset_kernel(CacheParams p) {
 // left the queue.  A ring slot that holds no entry keeps the K/V of its last
 // occupant (departures clear only the slot's metadata); other empty slots
 // were never written since the reset and hold zeros.
-constexpr int PF_THREADS = 256, PF_PER_THREAD = 4, PF_CHUNKS = PF_THREADS * PF_PER_THREAD;
+// one 16-byte chunk of K and one of V per thread: the most workgroups per
+// (stream, KV head) (kernel trace of the prompt hand-off on the Llama decode
+// geometry, 4096 tokens: 8.2 us per call, against 9.7 us with 4 per thread)
+constexpr int PF_THREADS = 256, PF_PER_THREAD = 1, PF_CHUNKS = PF_THREADS * PF_PER_THREAD;
 
 __global__ __launch_bounds__(PF_THREADS) void prefill_kernel(CacheParams p, const bf16* k, const bf16* v, int64_t ksb,
                                                       int64_t ksh, int64_t kst, int64_t vsb, int64_t vsh,
