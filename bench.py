@@ -8,9 +8,10 @@ One step = the whole path over one batch of synthetic input:
     d=128, a=4, s=64, n=256, 8192 tokens per stream, separators p=0.12):
     every token is pushed into and decoded against the cache of each of
     `--layers` layers (32 by default, as in Llama-3-8B), so the caches'
-    working set (~680 MB) exceeds the 256 MB Infinity Cache.  Tokens run as
-    replays of a HIP graph of 64 tokens; per-token K/V/q come from a pool of
-    64 inputs, the separator flags from the workload.
+    working set (~680 MB) exceeds the 256 MB Infinity Cache.  Each token has
+    its own q/k/v (N(0,1), drawn per step from the seed and resident on the
+    device before timing); tokens run as replays of a HIP graph of 64 tokens,
+    whose input buffers are refilled from the resident arrays per replay.
 
 Prints one JSON line.  `value` is the prefill leg's kept-FLOP rate (forward
 4*d*kept + backward 10*d*kept per q head, kept pairs counted by the mask
@@ -74,16 +75,53 @@ class PrefillLeg:
         return e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])
 
 
+def decode_lengths(wl: synth.DecodeWorkload, flags: np.ndarray, cap: int = 0) -> np.ndarray:
+    """Entries each stream's cache holds when step t attends, [T, B].  They
+    follow from the flags: sinks, separators that left the window queue (at
+    most s), and the queue, which holds the last L tokens: with P past-window
+    entries (capacity c = a + s + n + P) L counts up to n + P and then cycles
+    n, ..., n + P (a full queue empties to n - 1 before the next token)."""
+    T = flags.shape[0]
+    P = max(0, cap - (wl.a + wl.s + wl.n))
+    t = np.arange(T)
+    f = flags.astype(np.int64)
+    f_after_sinks = np.where(t[:, None] >= wl.a, f, 0)
+    csum = np.cumsum(f_after_sinks, axis=0)  # separators at positions <= t
+    x = np.maximum(t + 1 - wl.a, 0)  # tokens that entered the queue
+    L = np.where(x <= wl.n + P, x, wl.n + (x - wl.n - P - 1) % (P + 1))
+    last_left = t - L  # tokens at positions <= t - L have left the queue
+    left = np.where(last_left[:, None] >= 0, csum[np.clip(last_left, 0, None)], 0)
+    return np.minimum(t + 1, wl.a)[:, None] + np.minimum(left, wl.s) + L[:, None]
+
+
+def decode_bytes(wl: synth.DecodeWorkload, length: np.ndarray) -> float:
+    """Bytes one layer's decode must move over the steps of `length`: every
+    cached K and V row read once per token, plus q, o and the new K/V row (the
+    separator move is an implementation choice and not counted)."""
+    row = wl.Hkv * wl.d * 2
+    return float(length.sum()) * row * 2 + length.shape[0] * wl.B * (2 * wl.Hq * wl.d * 2 + 2 * row)
+
+
 class DecodeLeg:
     def __init__(self, wl: synth.DecodeWorkload, layers: int, seed: int = 0, cap: int = 0):
         self.wl, self.layers, self.cap = wl, layers, cap
         dev = "cuda"
         self.flags_np = wl.flags(seed)
         self.flags = torch.from_numpy(self.flags_np).to(dev)
-        k, v = wl.kv_steps(0, CHUNK, seed)
-        self.kp = torch.from_numpy(k).to(torch.bfloat16).to(dev)
-        self.vp = torch.from_numpy(v).to(torch.bfloat16).to(dev)
-        self.qp = torch.from_numpy(wl.q_steps(range(CHUNK), seed)).to(torch.bfloat16).to(dev)
+        # every token's own q, k, v (bf16), resident on the device
+        self.q_all = torch.empty((wl.T, wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device=dev)
+        self.k_all = torch.empty((wl.T, wl.B, wl.Hkv, wl.d), dtype=torch.bfloat16, device=dev)
+        self.v_all = torch.empty_like(self.k_all)
+        for t0 in range(0, wl.T, CHUNK):
+            t1 = min(wl.T, t0 + CHUNK)
+            k, v = wl.kv_steps(t0, t1, seed)
+            self.k_all[t0:t1].copy_(torch.from_numpy(k).to(torch.bfloat16))
+            self.v_all[t0:t1].copy_(torch.from_numpy(v).to(torch.bfloat16))
+            self.q_all[t0:t1].copy_(torch.from_numpy(wl.q_steps(range(t0, t1), seed)).to(torch.bfloat16))
+        # the graph's input buffers, refilled before each replay
+        self.kp = torch.empty((CHUNK,) + self.k_all.shape[1:], dtype=torch.bfloat16, device=dev)
+        self.vp = torch.empty_like(self.kp)
+        self.qp = torch.empty((CHUNK,) + self.q_all.shape[1:], dtype=torch.bfloat16, device=dev)
         self.scale = 1.0 / math.sqrt(wl.d)
         self.caches = [sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta, cap=cap) for _ in range(layers)]
         self.out = torch.empty((layers, wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device=dev)
@@ -103,36 +141,20 @@ class DecodeLeg:
         self.bytes = self._algorithmic_bytes()
 
     def _algorithmic_bytes(self) -> float:
-        """Bytes the path must move: every cached K and V row read once per
-        token, plus q, o and the new K/V row (the separator move is an
-        implementation choice and not counted).  Cache lengths follow from the
-        flags: sinks, separators that left the window queue (at most s), and
-        the queue, which holds the last L tokens: with P past-window entries
-        (capacity c = a + s + n + P) L counts up to n + P and then cycles
-        n, ..., n + P (a full queue empties to n - 1 before the next token)."""
-        wl = self.wl
-        T = wl.T
-        P = max(0, self.cap - (wl.a + wl.s + wl.n))
-        t = np.arange(T)
-        f = self.flags_np.astype(np.int64)
-        f_after_sinks = np.where(t[:, None] >= wl.a, f, 0)
-        csum = np.cumsum(f_after_sinks, axis=0)  # separators at positions <= t
-        x = np.maximum(t + 1 - wl.a, 0)  # tokens that entered the queue
-        L = np.where(x <= wl.n + P, x, wl.n + (x - wl.n - P - 1) % (P + 1))
-        last_left = t - L  # tokens at positions <= t - L have left the queue
-        left = np.where(last_left[:, None] >= 0, csum[np.clip(last_left, 0, None)], 0)
-        length = np.minimum(t + 1, wl.a)[:, None] + np.minimum(left, wl.s) + L[:, None]
-        row = wl.Hkv * wl.d * 2
-        per_layer = float(length.sum()) * row * 2 + T * wl.B * (2 * wl.Hq * wl.d * 2 + 2 * row)
+        length = decode_lengths(self.wl, self.flags_np, self.cap)
         self.mean_len = float(length.mean())
-        return per_layer * self.layers
+        return decode_bytes(self.wl, length) * self.layers
 
     def step(self):
         for c in self.caches:
             c.reset()
         self.ev[0].record()
         for ch in range(self.n_chunks):
-            self.fl_static.copy_(self.flags[ch * CHUNK:(ch + 1) * CHUNK])
+            sl = slice(ch * CHUNK, (ch + 1) * CHUNK)
+            self.fl_static.copy_(self.flags[sl])
+            self.kp.copy_(self.k_all[sl])
+            self.vp.copy_(self.v_all[sl])
+            self.qp.copy_(self.q_all[sl])
             self.graph.replay()
         self.ev[1].record()
 
@@ -140,33 +162,69 @@ class DecodeLeg:
         return self.ev[0].elapsed_time(self.ev[1])
 
 
-def cpu_baseline(leg: PrefillLeg, budget_s: float = 20.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the prefill
-    workload: the forward of one q head over all rows (kept keys only)."""
-    from oracle import sepllm_oracle as orc
-    wl = leg.wl
-    cores = len(os.sched_getaffinity(0))
-    q = leg.q[:, :1].float().cpu().numpy()
-    k = leg.k[:, :1].float().cpu().numpy()
-    v = leg.v[:, :1].float().cpu().numpy()
-    f = leg.mask.is_sep.cpu().numpy()
-    rows = wl.L
-    # shrink the sample if a first slice shows the budget would be exceeded
+def _rows_for_budget(run, L: int, first: int, budget_s: float) -> tuple[int, float]:
+    """Rows of the prefix sample: time `run(first)`, then grow the prefix so
+    that the timed call takes about budget_s (the work grows about as
+    rows^1.25 over this range: fixed costs weigh on short prefixes)."""
     t0 = time.perf_counter()
-    orc.attn_fwd(q[:, :, :2048], k[:, :, :2048], v[:, :, :2048], f[:, :2048], wl.a, wl.n, leg.scale)
+    run(first)
     t_small = time.perf_counter() - t0
-    est = t_small * (wl.L / 2048) ** 1.6
-    if est > budget_s:
-        rows = int(2048 * (budget_s / max(t_small, 1e-3)) ** (1 / 1.6)) // 256 * 256
-        rows = max(2048, min(wl.L, rows))
+    rows = int(first * (budget_s / max(t_small, 1e-3)) ** (1 / 1.25)) // 256 * 256
+    return max(first, min(L, rows)), t_small
+
+
+def cpu_baseline(pre: PrefillLeg, dwl: synth.DecodeWorkload, seed: int, budget_s: float = 8.0) -> dict:
+    """The fp64 oracle, as it stands, on bounded samples of the workloads,
+    timed on this host's cores: the forward and the backward of one q head
+    over a prefix of the L = 32768 sequence (a causal prefix is itself a
+    prefill of that length), and the decode simulation over the first steps
+    of the 16-stream decode with outputs over a window of steady-state steps.
+    Flags and inputs come from the seeded generators, never from the GPU."""
+    from oracle import sepllm_oracle as orc
+    wl = pre.wl
+    cores = len(os.sched_getaffinity(0))
+    f = orc.separator_flags(wl.tokens(seed), synth.SEP_IDS)
+    q, k, v = wl.qkv(seed)
+    bf = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).double().numpy()
+    q, k, v = bf(q[:, :1]), bf(k[:, :1]), bf(v[:, :1])
+    do = bf(wl.dout(seed)[:, :1])
+    sc = pre.scale
+    out = {}
+    fwd = lambda r: orc.attn_fwd(q[:, :, :r], k[:, :, :r], v[:, :, :r], f[:, :r], wl.a, wl.n, sc)
+    bwd = lambda r: orc.attn_bwd(q[:, :, :r], k[:, :, :r], v[:, :, :r], do[:, :, :r], f[:, :r], wl.a, wl.n, sc)
+    for name, run, per_pair in (("fwd", fwd, 4.0), ("bwd", bwd, 10.0)):
+        rows, _ = _rows_for_budget(run, wl.L, 2048, budget_s)
+        t0 = time.perf_counter()
+        run(rows)
+        dt = time.perf_counter() - t0
+        kept = int(orc.kept_pairs(f[:, :rows], wl.a, wl.n).sum())
+        out[name] = {"value": per_pair * wl.d * kept / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+                     "kind": "oracle",
+                     "sample": f"fp64 numpy {name} of 1 of {wl.Hq} q heads (d={wl.d}), rows 0..{rows - 1} "
+                               f"of {wl.L}: {kept} kept pairs in {dt:.1f} s"}
+    # decode: the simulator from an empty cache, outputs over steady-state steps
+    t_first, n_out = 800, 48
+    T = t_first + n_out
+    flags = dwl.flags(seed)[:T]
+    kk, vv = dwl.kv_steps(0, T, seed)
+    qq = dwl.q_steps(range(T), seed)
+    rnd = lambda x: torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    kk, vv, qq = rnd(kk), rnd(vv), rnd(qq)
+    steps = list(range(t_first, T))
     t0 = time.perf_counter()
-    orc.attn_fwd(q[:, :, :rows], k[:, :, :rows], v[:, :, :rows], f[:, :rows], wl.a, wl.n, leg.scale)
+    orc.decode_run(qq, kk, vv, flags, dwl.a, dwl.s, dwl.n, dwl.theta, dwl.shift, 1.0 / math.sqrt(dwl.d),
+                   out_steps=steps)
     dt = time.perf_counter() - t0
-    kept = int(orc.kept_pairs(f[:, :rows], wl.a, wl.n).sum())
-    flops = 4.0 * wl.d * kept
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"fp64 numpy forward of 1 of {wl.Hq} q heads, rows 0..{rows - 1} of {wl.L} "
-                      f"({kept} kept pairs, {dt:.1f} s)"}
+    nbytes = decode_bytes(dwl, decode_lengths(dwl, flags)[t_first:])
+    out["decode"] = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+                     "sample": f"fp64 numpy SepCache simulator, {dwl.B} streams x {T} steps from empty, outputs "
+                               f"of steps {t_first}..{T - 1} (one layer, {dwl.Hq}/{dwl.Hkv} heads, d={dwl.d}): "
+                               f"{nbytes / 1e6:.1f} MB of algorithmic bytes in {dt:.1f} s"}
+    fl = pre.fwd_flops / pre.kept_per_seq / wl.Hq, pre.bwd_flops / pre.kept_per_seq / wl.Hq
+    t_pair = fl[0] / (out["fwd"]["value"] * 1e12) + fl[1] / (out["bwd"]["value"] * 1e12)
+    return {"value": (fl[0] + fl[1]) / t_pair / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": "prefill forward + backward kept-FLOP rate combined from the two samples below",
+            "fwd": out["fwd"], "bwd": out["bwd"], "decode": out["decode"]}
 
 
 def kernel_sources_sha256() -> str:
@@ -230,8 +288,11 @@ def fixllm_leg(pre: PrefillLeg, delta: int, reps: int) -> dict:
             "fwd_util": round(fwd / PEAK_BF16_TFLOPS, 4), "bwd_util": round(bwd / PEAK_BF16_TFLOPS, 4)}
 
 
-def handoff_leg(wl: synth.DecodeWorkload, L: int, seed: int, reps: int = 50) -> dict:
-    """sepcache_prefill of an L-token prompt into one layer's caches.  Its
+def handoff_leg(wl: synth.DecodeWorkload, L: int, seed: int, sets: int = 8, rounds: int = 6) -> dict:
+    """sepcache_prefill of an L-token prompt into one layer's caches.  The
+    calls rotate over `sets` distinct (prompt K/V, cache) pairs, whose bytes
+    touched per call (~43 MB each) together exceed the 256 MB Infinity Cache,
+    so each call reads and writes HBM rather than cache-resident lines.  Its
     algorithmic bytes: the K/V rows of the entries kept (read once) and every
     slot's K/V and metadata and the counters (written once); the few mask
     words it reads per (stream, KV head) are left out."""
@@ -239,19 +300,20 @@ def handoff_leg(wl: synth.DecodeWorkload, L: int, seed: int, reps: int = 50) -> 
     tok = torch.from_numpy(synth.tokens_iid(seed, 90, wl.B, L, wl.p)).to(dev)
     m = sa.build_mask(tok, synth.SEP_IDS, wl.a, wl.n)
     gen = torch.Generator(device=dev).manual_seed(seed)
-    k = torch.randn((wl.B, wl.Hkv, L, wl.d), generator=gen, device=dev).to(torch.bfloat16)
-    v = torch.randn((wl.B, wl.Hkv, L, wl.d), generator=gen, device=dev).to(torch.bfloat16)
-    cache = sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta)
-    cache.prefill(k, v, m)
+    prompts = [tuple(torch.randn((wl.B, wl.Hkv, L, wl.d), generator=gen, device=dev).to(torch.bfloat16)
+                     for _ in range(2)) for _ in range(sets)]
+    caches = [sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta) for _ in range(sets)]
+    caches[0].prefill(*prompts[0], m)
     torch.cuda.synchronize()
-    entries = int((cache.slot_pos[:, 0] >= 0).sum())  # over streams, one KV head
-    # the reps run as one graph replay, back to back on the device: timed
+    entries = int((caches[0].slot_pos[:, 0] >= 0).sum())  # over streams, one KV head
+    # the calls run as one graph replay, back to back on the device: timed
     # call by call from Python, the host's launch rate would be measured
     stream = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
-        for _ in range(reps):
-            cache.prefill(k, v, m)
+        for _ in range(rounds):
+            for (k, v), c in zip(prompts, caches):
+                c.prefill(k, v, m)
     graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -259,10 +321,12 @@ def handoff_leg(wl: synth.DecodeWorkload, L: int, seed: int, reps: int = 50) -> 
     graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
+    calls = rounds * sets
+    us = e0.elapsed_time(e1) * 1e3 / calls
     row = wl.d * 2
-    nbytes = entries * wl.Hkv * row * 2 + wl.B * wl.Hkv * (cache.slots * (row * 2 + 5) + 32)
-    return {"config": {"B": wl.B, "Hkv": wl.Hkv, "d": wl.d, "a": wl.a, "s": wl.s, "n": wl.n, "prompt": L},
+    nbytes = entries * wl.Hkv * row * 2 + wl.B * wl.Hkv * (caches[0].slots * (row * 2 + 5) + 32)
+    return {"config": {"B": wl.B, "Hkv": wl.Hkv, "d": wl.d, "a": wl.a, "s": wl.s, "n": wl.n, "prompt": L,
+                       "distinct_sets": sets, "calls": calls},
             "us": round(us, 3), "bytes": nbytes, "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4), "entries": entries}
 
@@ -400,7 +464,8 @@ def main():
                         "p": wl.p, "separators": "clustered"},
             "decode": {"B": dec.wl.B, "Hq": dec.wl.Hq, "Hkv": dec.wl.Hkv, "d": dec.wl.d, "a": dec.wl.a,
                        "s": dec.wl.s, "n": dec.wl.n, "tokens": dec.wl.T, "p": dec.wl.p,
-                       "layers": args.layers, "shift": dec.wl.shift},
+                       "layers": args.layers, "shift": dec.wl.shift,
+                       "inputs": "each token its own q/k/v, N(0,1) per step from the seed, bf16, resident in HBM"},
         },
         "prefill": {
             "kept_pairs_per_head": pre.kept_per_seq,
@@ -447,7 +512,7 @@ def main():
     out["roofline"] = r_dec if t_dec > pre_ms else r_fwd
     out["rooflines"] = [r_fwd, r_bwd, r_dec]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(pre)
+        out["cpu_baseline"] = cpu_baseline(pre, synth.LLAMA_DECODE, args.seed)
     print(json.dumps(out), flush=True)
 
 

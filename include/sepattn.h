@@ -25,8 +25,10 @@
  *   - The return value is a status code (SEPATTN_OK = 0 or a negative error).
  *     Arguments are validated before any launch; on error nothing is
  *     enqueued and sepattn_last_error() gives a description (per thread).
- *   - Floating-point tensors are bf16 (SEPATTN_BF16) or fp32 (SEPATTN_F32);
- *     accumulation is fp32.  Head dimension d is 64 or 128.
+ *   - Floating-point tensors are bf16 (SEPATTN_BF16) or fp32 (SEPATTN_F32)
+ *     where a call takes a dtype (sepattn_fwd: both; sepattn_bwd: bf16 only,
+ *     SEPATTN_F32 gives SEPATTN_ENOTSUP); the SepCache is bf16.
+ *     Accumulation is fp32.  Head dimension d is 64 or 128.
  *   - Indices are 0-based.  a = number of sinks (initial tokens), n = window
  *     size, which counts the query itself: row i keeps j in (i-n, i].
  */
@@ -115,6 +117,26 @@ SEPATTN_API int sepattn_build_mask_fixed(int delta, const sepattn_mask* m, void*
  * bits: device uint32 [B, L, ceil(L/32)].  For testing; L <= 65536. */
 SEPATTN_API int sepattn_mask_bits(const sepattn_mask* m, uint32_t* bits, void* stream);
 
+/* Rows per query tile of sepattn_fwd (and of the dQ pass of sepattn_bwd)
+ * for window n: 64 for n <= 256, else 256.  -1 for n < 1. */
+SEPATTN_API int sepattn_fwd_tile_rows(int n);
+
+/* Per-query-tile descriptors: for the tile of rows [q0, q0 + tile_rows),
+ * q0 = t * tile_rows, the keys its rows see, in the order the forward and
+ * dQ kernels walk them ([ANTH] mask bullet):
+ *   desc[b][t][0] sink_vis = min(a, band_lo): sinks left of the band;
+ *   desc[b][t][1] sep_vis  = separators (j >= a) left of the band
+ *                            (sep_before[b][band_lo]);
+ *   desc[b][t][2] band_lo  = max(0, q0 - n + 1);
+ *   desc[b][t][3] band_hi  = min(L, q0 + tile_rows).
+ * Every key j < band_lo that some row of the tile keeps is one of those
+ * sink_vis + sep_vis anchors, kept by every row of the tile; keys in
+ * [band_lo, band_hi) take the element test.  The kernels derive these values
+ * on the fly from sep_before with the same device code; this call writes
+ * them out for checks.  desc: device int32 [B, ceil(L / tile_rows), 4];
+ * tile_rows >= 1.  One launch. */
+SEPATTN_API int sepattn_tile_desc(const sepattn_mask* m, int tile_rows, int32_t* desc, void* stream);
+
 /* ------------------------------------------------------------------------
  * Attention under M (prefill / training; [ANTH] mask bullet: the mask is
  * trained through, forward and backward).
@@ -137,6 +159,9 @@ typedef struct {
 
 /* O = softmax(scale * Q K^T restricted to M) V; lse[b,h,i] = natural
  * log-sum-exp of row i's kept scaled scores.  dtype applies to q, k, v, o.
+ * o_stride must keep the output rows apart (no two (b, h, l) rows may share
+ * an element, e.g. no zero stride on a dimension of extent > 1), else
+ * SEPATTN_EINVAL.
  * lse: device fp32 [B, Hq, L] contiguous, or NULL.  m must come from
  * sepattn_build_mask for the same B, L.  Every row keeps key j = i, so no row
  * is empty. */
@@ -151,7 +176,10 @@ SEPATTN_API size_t sepattn_bwd_workspace_size(const sepattn_shape* s);
  *   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
  *   dQ = scale dS K,  dK = scale dS^T Q,
  * dK/dV summed over the q heads of each KV head.  o and lse are the forward's
- * outputs; dout uses o's strides; dq, dk, dv are written (not accumulated).
+ * outputs; dout uses o's strides; dq, dk, dv are written (not accumulated)
+ * with the strides of q, k and v, which must therefore keep rows apart (as
+ * o_stride for sepattn_fwd), else SEPATTN_EINVAL.  dtype must be
+ * SEPATTN_BF16 (SEPATTN_F32: SEPATTN_ENOTSUP).
  * Deterministic: no atomics; every output row is written by one workgroup. */
 SEPATTN_API int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
                 const void* q, const void* k, const void* v, const void* o,

@@ -123,6 +123,28 @@ def separator_prefix(f: np.ndarray, a: int) -> np.ndarray:
     return out
 
 
+def tile_descriptors(f: np.ndarray, a: int, n: int, rows: int) -> np.ndarray:
+    """Per query tile of ``rows`` rows, [q0, q1), read off the mask M itself:
+    band_lo = max(0, q0 - n + 1) is the first key any row of the tile keeps
+    through its window and band_hi = q1; left of band_lo the tile keeps
+    exactly the keys every one of its rows keeps (checked here), counted as
+    sinks (j < a) and separators (j >= a).  Returns int32 [B, n_tiles, 4] of
+    (sink_vis, sep_vis, band_lo, band_hi).  [ANTH] mask bullet."""
+    B, L = f.shape
+    n_tiles = (L + rows - 1) // rows
+    out = np.zeros((B, n_tiles, 4), dtype=np.int32)
+    for b in range(B):
+        for t in range(n_tiles):
+            q0, q1 = t * rows, min(L, (t + 1) * rows)
+            lo = max(0, q0 - n + 1)
+            m = mask_rows(f[b], a, n, q0, q1, lo)  # rows of the tile, keys left of the band
+            seen = m.any(axis=0)
+            if not np.array_equal(seen, m.all(axis=0)):
+                raise AssertionError("a key left of the band is kept by some rows of the tile only")
+            out[b, t] = (int(seen[:a].sum()), int(seen[a:].sum()), lo, q1)
+    return out
+
+
 def kept_pairs(f: np.ndarray, a: int, n: int, block: int = 512) -> np.ndarray:
     """Number of kept (query, key) pairs per sequence: the popcount of M.
     int64 [B].  Rows are counted in groups of ``block``."""

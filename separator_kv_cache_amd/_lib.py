@@ -39,6 +39,8 @@ _SIGS = {
     "sepattn_mask_carve": (c_int, [POINTER(SepattnMask), c_int, c_int, c_int, c_int, c_void_p, c_size_t]),
     "sepattn_build_mask": (c_int, [c_void_p, POINTER(c_int32), c_int, POINTER(SepattnMask), c_void_p]),
     "sepattn_mask_bits": (c_int, [POINTER(SepattnMask), c_void_p, c_void_p]),
+    "sepattn_fwd_tile_rows": (c_int, [c_int]),
+    "sepattn_tile_desc": (c_int, [POINTER(SepattnMask), c_int, c_void_p, c_void_p]),
     "sepattn_fwd": (c_int, [POINTER(SepattnShape), c_int, POINTER(SepattnMask), c_void_p, c_void_p,
                             c_void_p, c_float, c_void_p, c_void_p, c_void_p]),
     "sepattn_bwd_workspace_size": (c_size_t, [POINTER(SepattnShape)]),

@@ -111,6 +111,20 @@ def mask_bits(m: Mask) -> torch.Tensor:
     return bits
 
 
+def fwd_tile_rows(n: int) -> int:
+    """sepattn_fwd_tile_rows: query rows per tile of the forward (and dQ)."""
+    return int(_lib.load().sepattn_fwd_tile_rows(int(n)))
+
+
+def tile_desc(m: Mask, tile_rows: int) -> torch.Tensor:
+    """sepattn_tile_desc: int32 [B, ceil(L / tile_rows), 4] of (sink_vis,
+    sep_vis, band_lo, band_hi) per query tile."""
+    n_tiles = (m.L + tile_rows - 1) // tile_rows
+    desc = torch.empty((m.B, n_tiles, 4), dtype=torch.int32, device=m.buffer.device)
+    check(_lib.load().sepattn_tile_desc(m.ref(), int(tile_rows), _ptr(desc), _stream()))
+    return desc
+
+
 def _shape(q, k, v, o) -> SepattnShape:
     for t in (q, k, v, o):
         if t.dim() != 4 or t.stride(-1) != 1:
@@ -147,8 +161,23 @@ def sepattn_fwd(q, k, v, m: Mask, scale: float | None = None, out: torch.Tensor 
     return o, lse
 
 
+def _rows_apart(t: torch.Tensor) -> bool:
+    """No two rows of a [B, H, L, d] tensor (last dimension contiguous) share
+    memory: the layout the ABI requires of an output."""
+    span = t.shape[-1]
+    for size, stride in sorted(((t.shape[i], t.stride(i)) for i in range(3) if t.shape[i] > 1),
+                               key=lambda x: x[1]):
+        if stride < span:
+            return False
+        span += (size - 1) * stride
+    return True
+
+
 def sepattn_bwd(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, workspace=None):
-    """sepattn_bwd: returns (dQ, dK, dV)."""
+    """sepattn_bwd: returns (dQ, dK, dV), laid out like q, k and v (a q, k or
+    v whose rows overlap, e.g. an expanded view, is copied to a contiguous
+    tensor first, since the gradients take its strides)."""
+    q, k, v = (t if _rows_apart(t) else t.contiguous() for t in (q, k, v))
     if dout.shape != o.shape or dout.stride() != o.stride():
         raise ValueError("dout must have o's shape and strides")
     if o.dtype != q.dtype or dout.dtype != q.dtype:

@@ -16,6 +16,7 @@ int sepattn_launch_build_mask_fixed(int delta, const sepattn_mask* m, hipStream_
 int sepattn_launch_build_mask(const int32_t* tok, const int32_t* ids, int n_ids, const sepattn_mask* m,
                               hipStream_t st);
 int sepattn_launch_mask_bits(const sepattn_mask* m, uint32_t* bits, hipStream_t st);
+int sepattn_launch_tile_desc(const sepattn_mask* m, int tile_rows, int32_t* desc, hipStream_t st);
 int sepattn_launch_fwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const void* q,
                        const void* k, const void* v, float scale, void* o, float* lse, hipStream_t st);
 int sepattn_launch_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const void* q,
@@ -136,6 +137,17 @@ int sepattn_mask_bits(const sepattn_mask* m, uint32_t* bits, void* stream) {
   return sepattn_launch_mask_bits(m, bits, (hipStream_t)stream);
 }
 
+int sepattn_fwd_tile_rows(int n) { return n < 1 ? -1 : fwd_tile_rows(n); }
+
+int sepattn_tile_desc(const sepattn_mask* m, int tile_rows, int32_t* desc, void* stream) {
+  g_err[0] = 0;
+  SEPATTN_TRY(check_mask(m, "tile_desc"));
+  if (!desc) return sepattn_fail(SEPATTN_EINVAL, "tile_desc: null output");
+  if (tile_rows < 1) return sepattn_fail(SEPATTN_EINVAL, "tile_desc: tile_rows=%d < 1", tile_rows);
+  SEPATTN_TRY(sepattn_check_device());
+  return sepattn_launch_tile_desc(m, tile_rows, desc, (hipStream_t)stream);
+}
+
 // ------------------------------------------------------------------ attention
 
 static int check_shape(const sepattn_shape* s, int dtype, const sepattn_mask* m, const char* who) {
@@ -170,11 +182,37 @@ static int check_shape(const sepattn_shape* s, int dtype, const sepattn_mask* m,
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// True when no two rows (b, h, l) of a [B, H, L, d] tensor with these
+// element strides (batch, head, token) and a contiguous last dimension share
+// an element: ordered by stride, every dimension of extent above one must
+// step past everything the smaller ones span.  Outputs must satisfy it, or
+// workgroups writing different rows would write the same memory.
+static bool rows_disjoint(const int64_t st[3], int B, int H, int L, int d) {
+  const int64_t ext[3] = {B, H, L};
+  int idx[3], k = 0;
+  for (int i = 0; i < 3; ++i)
+    if (ext[i] > 1) idx[k++] = i;
+  for (int i = 1; i < k; ++i)  // insertion sort by stride
+    for (int j = i; j > 0 && st[idx[j]] < st[idx[j - 1]]; --j) {
+      const int t = idx[j];
+      idx[j] = idx[j - 1];
+      idx[j - 1] = t;
+    }
+  int64_t span = d;  // elements one row covers, then everything below the next dimension
+  for (int i = 0; i < k; ++i) {
+    if (st[idx[i]] < span) return false;
+    span += (ext[idx[i]] - 1) * st[idx[i]];
+  }
+  return true;
+}
+
 int sepattn_fwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const void* q, const void* k,
                 const void* v, float scale, void* o, float* lse, void* stream) {
   g_err[0] = 0;
   SEPATTN_TRY(check_shape(s, dtype, m, "fwd"));
   if (!q || !k || !v || !o) return sepattn_fail(SEPATTN_EINVAL, "fwd: null tensor");
+  if (!rows_disjoint(s->o_stride, s->B, s->Hq, s->L, s->d))
+    return sepattn_fail(SEPATTN_EINVAL, "fwd: o_stride makes output rows overlap");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return sepattn_fail(SEPATTN_EINVAL, "fwd: tensors must be 16-byte aligned");
   if (!std::isfinite(scale)) return sepattn_fail(SEPATTN_EINVAL, "fwd: scale is not finite");
@@ -192,8 +230,13 @@ int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const 
                 void* dk, void* dv, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   SEPATTN_TRY(check_shape(s, dtype, m, "bwd"));
+  if (dtype != SEPATTN_BF16) return sepattn_fail(SEPATTN_ENOTSUP, "bwd: only bf16 is implemented");
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
     return sepattn_fail(SEPATTN_EINVAL, "bwd: null tensor or workspace");
+  // dQ, dK and dV are written with the strides of Q, K and V
+  if (!rows_disjoint(s->q_stride, s->B, s->Hq, s->L, s->d) || !rows_disjoint(s->k_stride, s->B, s->Hkv, s->L, s->d) ||
+      !rows_disjoint(s->v_stride, s->B, s->Hkv, s->L, s->d))
+    return sepattn_fail(SEPATTN_EINVAL, "bwd: q/k/v strides (also those of dq/dk/dv) make output rows overlap");
   const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv, workspace};
   for (const void* pp : ptrs)
     if (!aligned16(pp)) return sepattn_fail(SEPATTN_EINVAL, "bwd: tensors must be 16-byte aligned");

@@ -149,7 +149,30 @@ __global__ __launch_bounds__(256) void mask_bits_kernel(
     if (band_keep(i, j, a, n, fs)) row[j >> 5] |= 1u << (j & 31);
 }
 
+// One thread per query tile: the tile's descriptor as the forward and dQ
+// kernels derive it (tile_keys), for checks against the mask's definition.
+__global__ __launch_bounds__(256) void tile_desc_kernel(const int32_t* __restrict__ sep_before, int L, int a, int n,
+                                                        int tile_rows, int n_tiles, int32_t* __restrict__ desc) {
+  const int b = blockIdx.y;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_tiles) return;
+  const TileKeys k = tile_keys(t * tile_rows, tile_rows, L, a, n, sep_before + (size_t)b * (L + 1));
+  int32_t* o = desc + ((size_t)b * n_tiles + t) * 4;
+  o[0] = k.n_sink;
+  o[1] = k.n_gather - k.n_sink;
+  o[2] = k.band_lo;
+  o[3] = k.band_hi;
+}
+
 }  // namespace
+
+int sepattn_launch_tile_desc(const sepattn_mask* m, int tile_rows, int32_t* desc, hipStream_t st) {
+  const int n_tiles = (m->L + tile_rows - 1) / tile_rows;
+  dim3 grid((n_tiles + 255) / 256, m->B);
+  hipLaunchKernelGGL(tile_desc_kernel, grid, dim3(256), 0, st, m->sep_before, m->L, m->a, m->n, tile_rows,
+                     n_tiles, desc);
+  return sepattn_hip_check(hipGetLastError(), "tile_desc launch");
+}
 
 int sepattn_launch_build_mask(const int32_t* tok, const int32_t* ids, int n_ids, const sepattn_mask* m,
                               hipStream_t st) {

@@ -85,6 +85,24 @@ def test_argument_validation_without_gpu():
     s.q_stride[2] = 3
     assert lib.sepattn_fwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, 0.1, p, None, None) == _lib.EINVAL
     s = _shape()
+    s.o_stride[1] = 0  # every head's output rows on top of each other
+    assert lib.sepattn_fwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, 0.1, p, None, None) == _lib.EINVAL
+    assert b"overlap" in lib.sepattn_last_error()
+    s = _shape()
+    s.o_stride[2] = 32  # token rows of 64 elements, 32 apart
+    assert lib.sepattn_fwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, 0.1, p, None, None) == _lib.EINVAL
+    s = _shape()
+    s.o_stride[0], s.o_stride[1], s.o_stride[2] = 64, 64 * 1, 64 * 4  # [B, L, H, d] storage: rows apart
+    assert lib.sepattn_fwd(ctypes.byref(s), 7, ctypes.byref(m), p, p, p, 0.1, p, None, None) == _lib.ENOTSUP
+    s = _shape()
+    need = lib.sepattn_bwd_workspace_size(ctypes.byref(s))
+    assert lib.sepattn_bwd(ctypes.byref(s), _lib.F32, ctypes.byref(m), p, p, p, p, p, p, 0.1, p, p, p, p,
+                           need, None) == _lib.ENOTSUP  # the backward is bf16 only
+    s.k_stride[1] = 0  # dK would take K's strides: an expanded K is refused
+    assert lib.sepattn_bwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, p, p, p, 0.1, p, p, p, p,
+                           need, None) == _lib.EINVAL
+    assert b"overlap" in lib.sepattn_last_error()
+    s = _shape()
     need = lib.sepattn_bwd_workspace_size(ctypes.byref(s))
     assert need >= 1 * 4 * 64 * 4
     assert lib.sepattn_bwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, p, p, p, 0.1, p, p, p, p,
@@ -201,3 +219,17 @@ def test_binding_refuses_host_memory_and_bad_outputs():
         sa.sepattn_bwd(q, kv, kv, q, torch.zeros((1, 2, 32)), q[:, :1], m)
     with pytest.raises(ValueError, match="q's dtype"):
         sa.sepattn_bwd(q, kv, kv, q, torch.zeros((1, 2, 32)), q.float(), m)
+
+
+def test_binding_output_layouts():
+    """The gradients take the strides of q, k and v: the binding recognises
+    layouts whose rows overlap (an expanded view) and copies those inputs to
+    contiguous tensors before the backward."""
+    import torch
+    from separator_kv_cache_amd import binding as sa
+    kv = torch.zeros((2, 1, 32, 64), dtype=torch.bfloat16)
+    assert sa._rows_apart(kv)
+    assert not sa._rows_apart(kv.expand(2, 4, 32, 64))           # head stride 0
+    assert sa._rows_apart(torch.zeros((2, 32, 4, 64)).permute(0, 2, 1, 3))  # [B, L, H, d] storage
+    assert not sa._rows_apart(torch.zeros(256).as_strided((1, 1, 2, 64), (128, 128, 32, 1)))  # rows 32 apart
+    assert sa._rows_apart(torch.zeros((1, 1, 1, 64)).expand(3, 1, 1, 64)[:1])

@@ -117,11 +117,17 @@ def test_cache_steps_against_simulator(case):
 RUN = list(range(600, 624))
 
 
-def test_llama_decode_full_run_sampled():
-    wl = synth.LLAMA_DECODE
-    say("cache", wl.name)
+@pytest.mark.parametrize("shift", [True, False], ids=["shift", "original-positions"])
+def test_llama_decode_full_run_sampled(shift):
+    """The whole 8192-step Llama decode (16 streams, 32 q / 8 KV heads, d = 128,
+    a = 4, s = 64, n = 256) through the fused step, with positions shifted to
+    ranks in the cache and with original positions (plain RoPE, whose angles
+    reach 8191 times the base frequency at the last steps)."""
+    wl = synth.LLAMA_DECODE.with_(shift=shift)
+    say("cache", wl.name, "shift" if shift else "original positions")
     flags, kb, vb = _setup(wl)
-    sample = sorted({0, 1, 3, 4, 5, 100, 259, 260, 261, 793, 1500, 2048, 4095, 6000, 8191, *RUN})
+    sample = sorted({0, 1, 3, 4, 5, 100, 259, 260, 261, 793, 1500, 2048, 4095, 6000, 8000, 8001, 8100, 8190,
+                     8191, *RUN})
     qb = _bf(wl.q_steps(sample))
     kd, vd = kb.cuda(), vb.cuda()
     fd = torch.from_numpy(flags).cuda()
@@ -131,21 +137,21 @@ def test_llama_decode_full_run_sampled():
     outs = {}
     for t in range(wl.T):
         if t in sample:
-            outs[t] = cache.step(kd[t], vd[t], fd[t], qb[sample.index(t)].cuda(), sc, shift=True)
+            outs[t] = cache.step(kd[t], vd[t], fd[t], qb[sample.index(t)].cuda(), sc, shift=shift)
         else:
             cache.push(kd[t], vd[t], fd[t])
         for b in range(wl.B):
             sims[b].append(int(flags[t, b]))
             sims[b].evict()
         if t in sample:
-            if t in (0, 5, 261, 793, 4095, 8191) or t in RUN:
+            if t in (0, 5, 261, 793, 4095, 8000, 8191) or t in RUN:
                 torch.cuda.synchronize()
                 _check_state(cache, sims, kb, vb, t)
     torch.cuda.synchronize()
     assert all(len(s.order()) == wl.a + wl.s + wl.n for s in sims)
     qfull = np.zeros((wl.T, wl.B, wl.Hq, wl.d))
     qfull[sample] = as_f64(qb)
-    ref, _ = orc.decode_run(qfull, as_f64(kb), as_f64(vb), flags, wl.a, wl.s, wl.n, wl.theta, True, sc,
+    ref, _ = orc.decode_run(qfull, as_f64(kb), as_f64(vb), flags, wl.a, wl.s, wl.n, wl.theta, shift, sc,
                             out_steps=sample)
     for t in sample:
         assert max_abs(as_f64(outs[t]), ref[t]) <= TOL_BF16, t

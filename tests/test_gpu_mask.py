@@ -59,11 +59,14 @@ def test_mask_metadata_bit_exact(case):
         assert np.array_equal(m.kept.cpu().numpy(), orc.kept_pairs(f, a, n))
 
 
-BIT_CASES = [c for c in CASES if c[2] <= 4096]
+BIT_CASES = [c for c in CASES if c[2] <= 32768]
 
 
 @pytest.mark.parametrize("case", BIT_CASES, ids=[c[0] for c in BIT_CASES])
 def test_mask_expansion_matches_definition(case):
+    """The dense mask as the forward kernel's traversal walks it (gathered
+    anchors, then the band with its element test), every row, against the
+    definition; up to the L = 32768 Llama-shaped sequence."""
     name, B, L, a, n, p, clustered = case
     say("mask-bits", name)
     tok = (synth.tokens_clustered if clustered else synth.tokens_iid)(12, 41, B, L, p)
@@ -72,12 +75,33 @@ def test_mask_expansion_matches_definition(case):
     f = orc.separator_flags(tok, synth.SEP_IDS)
     W = (L + 31) // 32
     for b in range(B):
-        M = orc.mask_dense(f[b:b + 1], a, n)[0]
-        pad = np.zeros((L, W * 32), dtype=bool)
-        pad[:, :L] = M
-        want = np.packbits(pad.reshape(L, W, 32)[:, :, ::-1], axis=-1, bitorder="big")
-        want = want.view(">u4").reshape(L, W).astype(np.uint32)
-        assert np.array_equal(bits[b], want), (name, b)
+        for r0 in range(0, L, 1024):
+            r1 = min(L, r0 + 1024)
+            M = orc.mask_rows(f[b], a, n, r0, r1)
+            pad = np.zeros((r1 - r0, W * 32), dtype=bool)
+            pad[:, :L] = M
+            want = np.packbits(pad.reshape(r1 - r0, W, 32)[:, :, ::-1], axis=-1, bitorder="big")
+            want = want.view(">u4").reshape(r1 - r0, W).astype(np.uint32)
+            assert np.array_equal(bits[b, r0:r1], want), (name, b, r0)
+
+
+@pytest.mark.parametrize("case", BIT_CASES, ids=[c[0] for c in BIT_CASES])
+def test_tile_descriptors_bit_exact(case):
+    """Per-query-tile (sink_vis, sep_vis, band_lo, band_hi) as the kernels
+    derive them, against the oracle's reading of the mask: the forward's own
+    tile size for the window and other tile sizes (ragged last tiles)."""
+    name, B, L, a, n, p, clustered = case
+    say("tile-desc", name)
+    tok = (synth.tokens_clustered if clustered else synth.tokens_iid)(13, 43, B, L, p)
+    m = _gpu_mask(tok, a, n)
+    f = orc.separator_flags(tok, synth.SEP_IDS)
+    fwd_rows = sa.fwd_tile_rows(n)
+    assert fwd_rows == (64 if n <= 256 else 256)
+    sizes = [256] if L > 4096 else sorted({1, 7, 64, 256, fwd_rows})
+    for rows in sizes:
+        got = sa.tile_desc(m, rows).cpu().numpy()
+        want = orc.tile_descriptors(f, a, n, rows)
+        assert np.array_equal(got, want), (name, rows)
 
 
 def test_mask_deterministic():

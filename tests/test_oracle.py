@@ -125,6 +125,40 @@ def test_kept_pairs_popcount_matches_closed_form():
             assert kept[b] == _kept_closed_form(f[b], a, n)
 
 
+def test_tile_descriptors_closed_form_and_union():
+    """Tile descriptors against their closed form (sinks left of the band,
+    separators >= a left of it, by counting flags one by one) and against the
+    dense mask: a tile's rows together keep exactly the sink_vis + sep_vis
+    anchors left of band_lo plus what they keep in [band_lo, band_hi), and
+    nothing at or past band_hi.  Every flag pattern for L <= 8, and random
+    longer sequences with several tile sizes."""
+    cases = []
+    for L in range(1, 9):
+        for bits in range(1 << L):
+            cases.append((np.array([[(bits >> j) & 1 for j in range(L)]], dtype=np.uint8)))
+    rng = np.random.default_rng(5)
+    for L in (50, 97, 200):
+        cases.append((rng.random((2, L)) < 0.3).astype(np.uint8))
+    for f in cases:
+        B, L = f.shape
+        for a in sorted({0, 1, 3, L + 1}):
+            for n in sorted({1, 2, 5, L, L + 2}):
+                for rows in sorted({1, 3, 4, 64, L}):
+                    if L > 8 and rows == 3:
+                        continue
+                    got = orc.tile_descriptors(f, a, n, rows)
+                    M = orc.mask_dense(f, a, n)
+                    for b in range(B):
+                        for t in range(got.shape[1]):
+                            q0, q1 = t * rows, min(L, (t + 1) * rows)
+                            lo = max(0, q0 - n + 1)
+                            want = (min(a, lo), sum(int(f[b, j]) for j in range(a, lo)), lo, q1)
+                            assert tuple(got[b, t]) == want, (L, a, n, rows, b, t)
+                            seen = M[b, q0:q1].any(axis=0)
+                            assert int(seen[:lo].sum()) == want[0] + want[1]
+                            assert not seen[q1:].any()
+
+
 def test_separator_flags_membership():
     tok = np.array([[7, 8, 1013, 49999, 49998, 0, 4099]], dtype=np.int32)
     f = orc.separator_flags(tok, synth.SEP_IDS)

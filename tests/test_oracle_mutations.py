@@ -37,6 +37,10 @@ MISTAKES = [
     ("sinks listed as separators", "            if j >= a and f[b, j]:", "            if f[b, j]:"),
     ("LSE without the running maximum", "lse[b, h, r0:r1] = (mx + np.log(l))[:, 0]",
      "lse[b, h, r0:r1] = (np.log(l))[:, 0]"),
+    ("tile band starts one key early", "            lo = max(0, q0 - n + 1)\n            m = mask_rows",
+     "            lo = max(0, q0 - n)\n            m = mask_rows"),
+    ("tile anchors counted from the sinks' end", "out[b, t] = (int(seen[:a].sum()), int(seen[a:].sum()), lo, q1)",
+     "out[b, t] = (int(seen[:a].sum()), int(seen[a + 1:].sum()), lo, q1)"),
 ]
 
 
