@@ -187,6 +187,23 @@ SEPATTN_API int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mas
                 void* dq, void* dk, void* dv,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* sepattn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, with the D workspace in a static array that the
+ * library's code holds on each device (SEPATTN_BWD_NOALLOC_MAX_ROWS fp32
+ * values, 16 MiB, from the library's load until the process ends).  The call
+ * itself allocates nothing; the first call on a device looks up the array's
+ * address there.  B * Hq * L must not exceed SEPATTN_BWD_NOALLOC_MAX_ROWS,
+ * else SEPATTN_ESPACE.  Every call on a device shares its one array: calls
+ * that overlap on one device (different streams, or host threads without
+ * ordering) race and give wrong gradients.  Other arguments and errors as
+ * sepattn_bwd. */
+#define SEPATTN_BWD_NOALLOC_MAX_ROWS (1 << 22)
+SEPATTN_API int sepattn_bwd_noalloc(const sepattn_shape* s, int dtype, const sepattn_mask* m,
+                        const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, float scale,
+                        void* dq, void* dk, void* dv, void* stream);
+
 /* ------------------------------------------------------------------------
  * SepCache: the streaming cache ([PITH] key_machinery; [ANTH] streaming
  * bullet) with a sink block of a entries, a separator block of s entries kept

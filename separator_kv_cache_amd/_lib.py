@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(HERE, "libsepattn.so")
 OK, EINVAL, ENOTSUP, EHIP, ESPACE = 0, -1, -2, -3, -4
 F32, BF16 = 0, 1
 MAX_SEP_IDS = 64
+BWD_NOALLOC_MAX_ROWS = 1 << 22
 
 
 class SepattnMask(ctypes.Structure):
@@ -47,6 +48,9 @@ _SIGS = {
     "sepattn_bwd": (c_int, [POINTER(SepattnShape), c_int, POINTER(SepattnMask), c_void_p, c_void_p,
                             c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                             c_void_p, c_void_p, c_size_t, c_void_p]),
+    "sepattn_bwd_noalloc": (c_int, [POINTER(SepattnShape), c_int, POINTER(SepattnMask), c_void_p, c_void_p,
+                                    c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                    c_void_p, c_void_p]),
     "sepcache_slots": (c_int, [c_int, c_int, c_int, c_int]),
     "sepcache_k_rows": (c_int, [c_int]),
     "sepcache_reset": (c_int, [POINTER(SepCacheStruct), c_void_p]),

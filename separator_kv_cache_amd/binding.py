@@ -198,6 +198,31 @@ def sepattn_bwd(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, work
     return dq, dk, dv
 
 
+def sepattn_bwd_noalloc(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, dq=None, dk=None, dv=None):
+    """sepattn_bwd_noalloc: sepattn_bwd with the library's static workspace
+    (B * Hq * L <= BWD_NOALLOC_MAX_ROWS).  Outputs given by the caller are
+    written in place (the call then allocates nothing); missing ones are
+    allocated here like q, k and v."""
+    if dout.shape != o.shape or dout.stride() != o.stride():
+        raise ValueError("dout must have o's shape and strides")
+    if o.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("o and dout must have q's dtype")
+    s = _shape(q, k, v, o)
+    _check_lse(lse, s.B, s.Hq, s.L)
+    outs = []
+    for g, t in ((dq, q), (dk, k), (dv, v)):
+        if g is None:
+            g = torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+        elif g.shape != t.shape or g.stride() != t.stride() or g.dtype != t.dtype:
+            raise ValueError("gradient outputs must match q, k and v in shape, strides and dtype")
+        outs.append(g)
+    sc = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
+    check(_lib.load().sepattn_bwd_noalloc(ctypes.byref(s), _DT[q.dtype], m.ref(), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(o), _ptr(lse), _ptr(dout), sc, _ptr(outs[0]), _ptr(outs[1]),
+                                          _ptr(outs[2]), _stream()))
+    return tuple(outs)
+
+
 class SepCache:
     """A SepCache for B streams (bf16 K/V); cap is the capacity c (0 or
     a + s + n: no past window)."""

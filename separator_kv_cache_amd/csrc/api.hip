@@ -22,6 +22,9 @@ int sepattn_launch_fwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
 int sepattn_launch_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const void* q,
                        const void* k, const void* v, const void* o, const float* lse, const void* dout,
                        float scale, void* dq, void* dk, void* dv, float* dsum, hipStream_t st);
+int sepattn_launch_bwd_noalloc(const sepattn_shape* s, int dtype, const sepattn_mask* m, const void* q,
+                               const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                               float scale, void* dq, void* dk, void* dv, hipStream_t st);
 int sepcache_launch_reset(const sepcache* c, hipStream_t st);
 int sepcache_launch_update(const sepcache* c, const void* k_new, const void* v_new, const uint8_t* is_sep,
                            int do_append, int do_evict, hipStream_t st);
@@ -247,6 +250,29 @@ int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const 
   SEPATTN_TRY(sepattn_check_device());
   return sepattn_launch_bwd(s, dtype, m, q, k, v, o, lse, dout, scale, dq, dk, dv, (float*)workspace,
                             (hipStream_t)stream);
+}
+
+int sepattn_bwd_noalloc(const sepattn_shape* s, int dtype, const sepattn_mask* m, const void* q, const void* k,
+                        const void* v, const void* o, const float* lse, const void* dout, float scale, void* dq,
+                        void* dk, void* dv, void* stream) {
+  g_err[0] = 0;
+  SEPATTN_TRY(check_shape(s, dtype, m, "bwd_noalloc"));
+  if (dtype != SEPATTN_BF16) return sepattn_fail(SEPATTN_ENOTSUP, "bwd_noalloc: only bf16 is implemented");
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return sepattn_fail(SEPATTN_EINVAL, "bwd_noalloc: null tensor");
+  const void* ptrs[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* pp : ptrs)
+    if (!aligned16(pp)) return sepattn_fail(SEPATTN_EINVAL, "bwd_noalloc: tensors must be 16-byte aligned");
+  if (!rows_disjoint(s->q_stride, s->B, s->Hq, s->L, s->d) || !rows_disjoint(s->k_stride, s->B, s->Hkv, s->L, s->d) ||
+      !rows_disjoint(s->v_stride, s->B, s->Hkv, s->L, s->d))
+    return sepattn_fail(SEPATTN_EINVAL, "bwd_noalloc: q/k/v strides (also those of dq/dk/dv) make output rows overlap");
+  const int64_t rows = (int64_t)s->B * s->Hq * s->L;
+  if (rows > SEPATTN_BWD_NOALLOC_MAX_ROWS)
+    return sepattn_fail(SEPATTN_ESPACE, "bwd_noalloc: B*Hq*L = %lld rows exceed the static workspace's %d",
+                        (long long)rows, SEPATTN_BWD_NOALLOC_MAX_ROWS);
+  if (!std::isfinite(scale)) return sepattn_fail(SEPATTN_EINVAL, "bwd_noalloc: scale is not finite");
+  SEPATTN_TRY(sepattn_check_device());
+  return sepattn_launch_bwd_noalloc(s, dtype, m, q, k, v, o, lse, dout, scale, dq, dk, dv, (hipStream_t)stream);
 }
 
 // ------------------------------------------------------------------ SepCache

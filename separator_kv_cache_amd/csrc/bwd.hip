@@ -13,6 +13,7 @@
 //    keys of one class and walks the rows that can see them: [first key, L)
 //    for anchors, [first key, last key + n) for plain keys, summing over the
 //    q heads of its KV head.
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -618,6 +619,49 @@ int launch_dkdv(const BwdParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+// The workspace of sepattn_bwd_noalloc: D for up to SEPATTN_BWD_NOALLOC_MAX_ROWS
+// rows, a file-scope array that each device holds from the moment this
+// library's code is loaded on it until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is a stand-in, not a
+// device address): it looks the address up once per device and passes that.
+static __device__ __align__(256) float scratch[SEPATTN_BWD_NOALLOC_MAX_ROWS];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// The device address of `scratch` on the current device (looked up on the
+// first call per device, with that device current).
+static int scratch_address(float** out) {
+  int dev = 0;
+  SEPATTN_TRY(sepattn_hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  if (dev < 0 || dev >= kMaxDevices) return sepattn_fail(SEPATTN_ENOTSUP, "bwd_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    SEPATTN_TRY(sepattn_hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    g_scratch_ptr[dev] = (float*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SEPATTN_OK;
+}
+
+int sepattn_launch_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const void* q, const void* k,
+                       const void* v, const void* o, const float* lse, const void* dout, float scale, void* dq,
+                       void* dk, void* dv, float* dsum, hipStream_t st);
+
+int sepattn_launch_bwd_noalloc(const sepattn_shape* s, int dtype, const sepattn_mask* m, const void* q,
+                               const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                               float scale, void* dq, void* dk, void* dv, hipStream_t st) {
+  float* ws = nullptr;
+  SEPATTN_TRY(scratch_address(&ws));
+  // D is written for every row by the dQ kernel before the dK/dV kernel
+  // reads it, so nothing needs clearing between calls
+  return sepattn_launch_bwd(s, dtype, m, q, k, v, o, lse, dout, scale, dq, dk, dv, ws, st);
+}
 
 int sepattn_launch_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const void* q, const void* k,
                        const void* v, const void* o, const float* lse, const void* dout, float scale, void* dq,

@@ -102,6 +102,18 @@ def test_argument_validation_without_gpu():
     assert lib.sepattn_bwd(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, p, p, p, 0.1, p, p, p, p,
                            need, None) == _lib.EINVAL
     assert b"overlap" in lib.sepattn_last_error()
+    # the no-allocation backward: its static workspace bounds B * Hq * L
+    mb, _keep_b = _mask(L=2048)
+    s = _shape(Hq=4096, Hkv=1, L=2048)
+    assert 4096 * 2048 > _lib.BWD_NOALLOC_MAX_ROWS
+    assert lib.sepattn_bwd_noalloc(ctypes.byref(s), _lib.BF16, ctypes.byref(mb), p, p, p, p, p, p, 0.1, p, p, p,
+                                   None) == _lib.ESPACE
+    assert b"static workspace" in lib.sepattn_last_error()
+    s = _shape()
+    assert lib.sepattn_bwd_noalloc(ctypes.byref(s), _lib.F32, ctypes.byref(m), p, p, p, p, p, p, 0.1, p, p, p,
+                                   None) == _lib.ENOTSUP
+    assert lib.sepattn_bwd_noalloc(ctypes.byref(s), _lib.BF16, ctypes.byref(m), p, p, p, p, p, p, 0.1, None, p, p,
+                                   None) == _lib.EINVAL
     s = _shape()
     need = lib.sepattn_bwd_workspace_size(ctypes.byref(s))
     assert need >= 1 * 4 * 64 * 4
