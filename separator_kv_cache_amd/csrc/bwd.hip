@@ -55,14 +55,21 @@ struct BwdParams {
 
 // Row strides of tiles read both by 16-byte row reads (MFMA operands along a
 // row) and by transposing reads: an odd number of 16-byte chunks keeps the
-// row reads of 16 lanes on distinct banks, and 19 chunks (D = 128) puts the
-// four rows of a transposing read of 16 lanes on disjoint bank windows.
+// row reads of 16 lanes on distinct banks (the stride at d = 64).
 template <int D>
 constexpr int dual_read_stride() { return D == 128 ? 152 : 88; }
 
+// dQ's K and V tiles.  At d = 128 the rows are 160 elements apart, which
+// keeps the four rows of a transposing read of K (dQ's A operand) in
+// distinct banks, and chunk c of row r sits at chunk position
+// c ^ ((r >> 2) & 3), which spreads the 16 rows of a row read (S and dP) over
+// all banks too (the layout of dK/dV's Q/dO tiles below).  At d = 64 the
+// stride is padded instead.
 template <int D>
 struct DqLayout {
-  static constexpr int STR = dual_read_stride<D>();
+  static constexpr bool SWZ = D == 128;
+  static constexpr int STR = SWZ ? 160 : dual_read_stride<D>();
+  __device__ static int tau(int r) { return SWZ ? (r >> 2) & 3 : 0; }
   static constexpr int K_BYTES = BK * STR * 2;
   static constexpr int BUF_BYTES = 2 * K_BYTES + 16;  // K, V, separator bits
 };
@@ -135,8 +142,8 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
     if (wave == 0) flag = ks.flag_byte(t, lane);
   };
   auto store = [&](int s) {
-    mk.template store<STR>(kbuf(s));
-    mv.template store<STR>(vbuf(s));
+    mk.template store<STR, LY::SWZ>(kbuf(s));
+    mv.template store<STR, LY::SWZ>(vbuf(s));
     if (wave == 0) {
       const uint64_t bits = __ballot(flag != 0);
       if (lane == 0) *fbuf(s) = bits;
@@ -163,9 +170,12 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
     // after the first MFMAs, so their address work runs beside the matrix
     // core instead of in front of it.
     constexpr int NSD = 2 * NKK * NKB, PD = 4;
+    // row x * 32 + qn, chunk c = 2 kk + hh at position 4 (c >> 2) + ((c & 3) ^ tau)
+    const int ta = LY::tau(qn);
     auto opnd = [&](int i) -> bf16x8 {
       const int kk = i / (2 * NKB), x = (i >> 1) % NKB;
-      return *(const bf16x8*)(((i & 1) ? vt : kt) + (x * 32 + qn) * STR + kk * 16 + hh * 8);
+      const int pos = 4 * (kk >> 1) + ((2 * (kk & 1) + hh) ^ ta);
+      return *(const bf16x8*)(((i & 1) ? vt : kt) + (x * 32 + qn) * STR + pos * 8);
     };
     f32x16 sacc[NKB], dpacc[NKB];
 #pragma unroll
@@ -194,8 +204,13 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
       for (int r = 0; r < 16; ++r)
         sacc[x][r] = fast_exp2(__builtin_fmaf(sacc[x][r], p.scale_log2, -lse2)) * (dpacc[x][r] - Dv);
 
-    // dQ^T += K^T dS^T (K^T through LDS transposing reads)
+    // dQ^T += K^T dS^T (K^T through LDS transposing reads): rows kr and
+    // kr + 8 (tau (g >> 1) and (g >> 1) + 2), chunk 4 db + clo
     const int g = lane >> 4, li = lane & 15;
+    const int clo = 2 * (g & 1) + ((li & 3) >> 1);
+    const int kr0 = 4 * (g >> 1) + (li >> 2);
+    const int tr_lo = kr0 * STR + (clo ^ LY::tau(kr0)) * 8 + 4 * (li & 1);
+    const int tr_hi = (kr0 + 8) * STR + (clo ^ LY::tau(kr0 + 8)) * 8 + 4 * (li & 1);
 #pragma unroll
     for (int c = 0; c < BK / 16; ++c) {
       bf16x8 bsv;
@@ -203,10 +218,8 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
       for (int s = 0; s < 8; ++s) bsv[s] = (bf16)sacc[c >> 1][(c & 1) * 8 + s];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const int dim = db * 32 + 16 * (g & 1) + 4 * (li & 3);
-        const int kr = 16 * c + 4 * (g >> 1) + (li >> 2);
-        const bf16x4 lo = lds_read_tr16(kt + kr * STR + dim);
-        const bf16x4 hi = lds_read_tr16(kt + (kr + 8) * STR + dim);
+        const bf16x4 lo = lds_read_tr16(kt + 16 * c * STR + 32 * db + tr_lo);
+        const bf16x4 hi = lds_read_tr16(kt + 16 * c * STR + 32 * db + tr_hi);
         const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         dqacc[db] = mfma32x16(a, bsv, dqacc[db]);
       }

@@ -135,11 +135,17 @@ struct RowMover {
     for (int u = 0; u < PT; ++u)
       r[u] = bld16(rs, key[u] >= 0 ? (uint32_t)key[u] * row_bytes + chunk() * 16 : BUF_OOB);
   }
-  template <int STR>
+  // SWZ: chunk c of row r goes to chunk position c ^ ((r >> 2) & 3) (the
+  // reader applies the same map).
+  template <int STR, bool SWZ = false>
   __device__ __forceinline__ void store(T* dst) const {
+    const int r0 = (int)threadIdx.x / CH;
 #pragma unroll
-    for (int u = 0; u < PT; ++u)
-      st16((char*)(dst + ((int)threadIdx.x / CH + u * ROWS_PER_PASS) * STR) + chunk() * 16, r[u]);
+    for (int u = 0; u < PT; ++u) {
+      const int row = r0 + u * ROWS_PER_PASS;
+      const int pos = SWZ ? chunk() ^ ((row >> 2) & 3) : chunk();
+      st16((char*)(dst + row * STR) + pos * 16, r[u]);
+    }
   }
 };
 
