@@ -173,10 +173,30 @@ def _rows_apart(t: torch.Tensor) -> bool:
     return True
 
 
-def sepattn_bwd(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, workspace=None):
+def bwd_workspace_bytes(q, k, v, o) -> int:
+    """sepattn_bwd_workspace_size for these tensors."""
+    return int(_lib.load().sepattn_bwd_workspace_size(ctypes.byref(_shape(q, k, v, o))))
+
+
+def _grad_outputs(grads, q, k, v):
+    """dq, dk, dv laid out like q, k, v: the caller's tensors (checked) or new ones."""
+    outs = []
+    for g, t in zip(grads, (q, k, v)):
+        if g is None:
+            g = torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+        elif g.shape != t.shape or g.stride() != t.stride() or g.dtype != t.dtype:
+            raise ValueError("gradient outputs must match q, k and v in shape, strides and dtype")
+        outs.append(g)
+    return outs
+
+
+def sepattn_bwd(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, workspace=None,
+                dq=None, dk=None, dv=None):
     """sepattn_bwd: returns (dQ, dK, dV), laid out like q, k and v (a q, k or
     v whose rows overlap, e.g. an expanded view, is copied to a contiguous
-    tensor first, since the gradients take its strides)."""
+    tensor first, since the gradients take its strides).  Outputs and a
+    workspace given by the caller are used in place (a loop that passes them
+    allocates nothing)."""
     q, k, v = (t if _rows_apart(t) else t.contiguous() for t in (q, k, v))
     if dout.shape != o.shape or dout.stride() != o.stride():
         raise ValueError("dout must have o's shape and strides")
@@ -188,9 +208,7 @@ def sepattn_bwd(q, k, v, o, lse, dout, m: Mask, scale: float | None = None, work
     need = lib.sepattn_bwd_workspace_size(ctypes.byref(s))
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
-    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
-    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+    dq, dk, dv = _grad_outputs((dq, dk, dv), q, k, v)
     sc = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
     check(lib.sepattn_bwd(ctypes.byref(s), _DT[q.dtype], m.ref(), _ptr(q), _ptr(k), _ptr(v),
                           _ptr(o), _ptr(lse), _ptr(dout), sc, _ptr(dq), _ptr(dk), _ptr(dv),
@@ -209,13 +227,7 @@ def sepattn_bwd_noalloc(q, k, v, o, lse, dout, m: Mask, scale: float | None = No
         raise ValueError("o and dout must have q's dtype")
     s = _shape(q, k, v, o)
     _check_lse(lse, s.B, s.Hq, s.L)
-    outs = []
-    for g, t in ((dq, q), (dk, k), (dv, v)):
-        if g is None:
-            g = torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
-        elif g.shape != t.shape or g.stride() != t.stride() or g.dtype != t.dtype:
-            raise ValueError("gradient outputs must match q, k and v in shape, strides and dtype")
-        outs.append(g)
+    outs = _grad_outputs((dq, dk, dv), q, k, v)
     sc = 1.0 / math.sqrt(q.shape[-1]) if scale is None else float(scale)
     check(_lib.load().sepattn_bwd_noalloc(ctypes.byref(s), _DT[q.dtype], m.ref(), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(o), _ptr(lse), _ptr(dout), sc, _ptr(outs[0]), _ptr(outs[1]),
