@@ -128,6 +128,8 @@ class DecodeLeg:
         self.caches = [sa.SepCache(wl.B, wl.Hkv, wl.d, wl.a, wl.s, wl.n, wl.theta, cap=cap) for _ in range(layers)]
         self.out = torch.empty((layers, wl.B, wl.Hq, wl.d), dtype=torch.bfloat16, device=dev)
         self.fl_static = torch.zeros((CHUNK, wl.B), dtype=torch.uint8, device=dev)
+        for c in self.caches:  # each cache's step workspace, zero-filled before the graph is captured
+            c.workspace(wl.Hq)
         torch.cuda.synchronize()
         self.stream = torch.cuda.Stream()
         self.graph = torch.cuda.CUDAGraph()
