@@ -169,7 +169,8 @@ SEPATTN_API int sepattn_fwd(const sepattn_shape* s, int dtype, const sepattn_mas
                 const void* q, const void* k, const void* v, float scale,
                 void* o, float* lse, void* stream);
 
-/* Workspace bytes for sepattn_bwd (fp32 D = rowsum(dO * O), [B, Hq, L]). */
+/* Workspace bytes for sepattn_bwd: fp32 D = rowsum(dO * O), [B, Hq, L], then
+ * 1 KiB of counters that assign the dK/dV kernel's key tiles to workgroups. */
 SEPATTN_API size_t sepattn_bwd_workspace_size(const sepattn_shape* s);
 
 /* Gradients for upstream dO: with P the masked softmax,
@@ -180,7 +181,8 @@ SEPATTN_API size_t sepattn_bwd_workspace_size(const sepattn_shape* s);
  * with the strides of q, k and v, which must therefore keep rows apart (as
  * o_stride for sepattn_fwd), else SEPATTN_EINVAL.  dtype must be
  * SEPATTN_BF16 (SEPATTN_F32: SEPATTN_ENOTSUP).
- * Deterministic: no atomics; every output row is written by one workgroup. */
+ * Deterministic: every output row is written by one workgroup; the only
+ * atomics choose which workgroup computes which key tile. */
 SEPATTN_API int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
                 const void* q, const void* k, const void* v, const void* o,
                 const float* lse, const void* dout, float scale,
@@ -189,9 +191,10 @@ SEPATTN_API int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mas
 
 /* sepattn_bwd for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
- * same kernels and results, with the D workspace in a static array that the
+ * same kernels and results, with the workspace in a static array that the
  * library's code holds on each device (SEPATTN_BWD_NOALLOC_MAX_ROWS fp32
- * values, 16 MiB, from the library's load until the process ends).  The call
+ * values of D, 16 MiB, and 1 KiB of counters, from the library's load until
+ * the process ends).  The call
  * itself allocates nothing; the first call on a device looks up the array's
  * address there.  B * Hq * L must not exceed SEPATTN_BWD_NOALLOC_MAX_ROWS,
  * else SEPATTN_ESPACE.  Every call on a device shares its one array: calls

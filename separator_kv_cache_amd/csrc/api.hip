@@ -225,7 +225,7 @@ int sepattn_fwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const 
 
 size_t sepattn_bwd_workspace_size(const sepattn_shape* s) {
   if (!s || s->B <= 0 || s->Hq <= 0 || s->L <= 0) return 0;
-  return align256((size_t)s->B * s->Hq * s->L * 4);
+  return sepattn_bwd_d_bytes(s) + SEPATTN_BWD_QUEUE_BYTES;
 }
 
 int sepattn_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m, const void* q, const void* k,

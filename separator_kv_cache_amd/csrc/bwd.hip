@@ -4,7 +4,7 @@
 // With P the masked softmax and D_i = sum_d dO_i O_i:
 //   dV = P^T dO,  dP = dO V^T,  dS = P (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Two kernels, no atomics, every output row written by one workgroup:
+// Two kernels, every output row written by one workgroup:
 //  * dq_kernel: query-major, the forward's traversal (gathered anchors, then
 //    the band).  Its prologue computes D for its rows and stores it.
 //  * dkdv_kernel: key-major.  Keys are split into two compacted classes:
@@ -12,7 +12,10 @@
 //    plain tokens, which only rows within n see.  A workgroup owns 32*WAVES
 //    keys of one class and walks the rows that can see them: [first key, L)
 //    for anchors, [first key, last key + n) for plain keys, summing over the
-//    q heads of its KV head.
+//    q heads of its KV head.  Which workgroup takes which key tile is decided
+//    when it starts, from a counter per XCD (the only atomics); the results do
+//    not depend on it.
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -29,6 +32,7 @@ struct BwdParams {
   const float* lse;
   bf16 *dq, *dk, *dv;
   float* dsum;  // D [B, Hq, L]
+  uint32_t* queue;  // dkdv: the next key tile of each XCD's range (8 counters, 128 bytes apart)
   int64_t sq[3], sk[3], sv[3], so[3];
   uint32_t k_span, v_span;  // bytes of one (sequence, KV head) slice of K, V
   uint32_t q_span, o_span;  // bytes of one (sequence, q head) slice of Q (dQ), O (dO)
@@ -119,6 +123,9 @@ __global__ __launch_bounds__(WAVES * 64) void dq_kernel(BwdParams p) {
   const size_t rowid = ((size_t)b * p.Hq + h) * p.L + (row_ok ? my_row : 0);
   const float lse2 = row_ok ? p.lse[rowid] * 1.4426950408889634f : 0.f;
   if (row_ok && hh == 0) p.dsum[rowid] = Dv;
+  // the dK/dV kernel that follows takes its key tiles from these counters
+  if (blockIdx.x == 0 && threadIdx.x < 8)
+    __hip_atomic_store(p.queue + 32 * threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   using MV = RowMover<bf16, D, NT>;
   constexpr int PT = MV::PT;
@@ -299,8 +306,9 @@ struct DkvLayout {
   static_assert(SMEM <= 160 * 1024, "dK/dV tiles exceed the LDS of a workgroup");
 };
 
+// One key tile of the dK/dV pass: logical tile lam (below).
 template <int D>
-__global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void dkdv_tile(const BwdParams& p, int lam) {
   using LY = DkvLayout<D>;
   constexpr int KT = 128, STR = LY::STR, PSTR = LY::PSTR;
   constexpr int NKK = D / 16;          // 16-dim steps of S and dP
@@ -315,13 +323,7 @@ __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kg = wave >> 1, hf = wave & 1, half = wave >> 2;
   const int ht = (int)threadIdx.x & (HT - 1);
-  // XCD-aware order (as tile_work): the key tiles of one (sequence, KV head)
-  // run on one XCD, anchor tiles (the longest row ranges) first.  (Spreading
-  // one head over all XCDs instead, to share the Infinity Cache, measured
-  // slower and with more L2 misses.)
   const int per = 2 * p.n_key_tiles;
-  const int N = p.B * p.Hkv * per;
-  const int lam = (N % 8 == 0) ? ((int)blockIdx.x % 8) * (N / 8) + (int)blockIdx.x / 8 : (int)blockIdx.x;
   const int bk = lam / per, rem = lam % per;
   const int b = bk / p.Hkv, kvh = bk % p.Hkv;
   const bool anchors = rem < p.n_key_tiles;
@@ -611,6 +613,45 @@ __global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
   }
 }
 
+// Persistent: one workgroup per compute unit, each taking key tiles until
+// none is left.  Logical tiles: B * Hkv * 2 * n_key_tiles, (sequence, KV
+// head) major, anchor tiles (the longest row ranges, longest first) before
+// plain ones; when their number divides by 8, XCD x owns the range
+// [x N/8, (x+1) N/8), so the key tiles of one (sequence, KV head) run on one
+// XCD and share its L2 (spreading a head over all XCDs, to share the
+// Infinity Cache instead, measured slower with more L2 misses).  A workgroup
+// takes the next tile of its XCD's range from that range's counter, then of
+// the other ranges once its own is exhausted: every tile is taken once, and
+// the compute units of an XCD run its tiles longest first, each starting the
+// next one as it finishes (launching one workgroup per tile instead left the
+// order in which compute units receive workgroups to the dispatcher, which
+// does not follow which ones are free: about 9 % of the pass was idle time).
+// The counters are zeroed by the dQ kernel, which runs first.
+template <int D>
+__global__ __launch_bounds__(512) void dkdv_kernel(BwdParams p) {
+  const int N = p.B * p.Hkv * 2 * p.n_key_tiles;
+  const int R = N % 8 == 0 ? 8 : 1;  // ranges
+  const int len = N / R;
+  const int x = R == 8 ? (int)__builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 7 : 0;  // XCC_ID[3:0]
+  __shared__ int pick;
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int job = -1;
+      for (int r = 0; r < R && job < 0; ++r) {
+        const int xr = (x + r) % R;
+        const uint32_t k = __hip_atomic_fetch_add(p.queue + 32 * xr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (k < (uint32_t)len) job = xr * len + (int)k;
+      }
+      pick = job;
+    }
+    __syncthreads();
+    const int lam = pick;
+    __syncthreads();  // read by every wave before the next tile's pick
+    if (lam < 0) break;
+    dkdv_tile<D>(p, lam);
+  }
+}
+
 template <int D, int WAVES>
 int launch_dq(const BwdParams& p, hipStream_t st) {
   const int smem = 2 * DqLayout<D>::BUF_BYTES;
@@ -627,18 +668,23 @@ int launch_dkdv(const BwdParams& p, hipStream_t st) {
   auto kern = dkdv_kernel<D>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
   if (e != hipSuccess) return sepattn_hip_check(e, "dkdv smem attribute");
-  hipLaunchKernelGGL(kern, dim3(p.B * p.Hkv * 2 * p.n_key_tiles), dim3(512), smem, st, p);
+  int dev = 0, cus = 0;
+  SEPATTN_TRY(sepattn_hip_check(hipGetDevice(&dev), "hipGetDevice"));
+  SEPATTN_TRY(sepattn_hip_check(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev),
+                                "compute unit count"));
+  const int tiles = p.B * p.Hkv * 2 * p.n_key_tiles;
+  hipLaunchKernelGGL(kern, dim3(std::max(1, std::min(tiles, cus))), dim3(512), smem, st, p);
   return sepattn_hip_check(hipGetLastError(), "dkdv launch");
 }
 
 }  // namespace
 
 // The workspace of sepattn_bwd_noalloc: D for up to SEPATTN_BWD_NOALLOC_MAX_ROWS
-// rows, a file-scope array that each device holds from the moment this
+// rows and the dK/dV tile counters, a file-scope array that each device holds from the moment this
 // library's code is loaded on it until the process ends.  Host code never
 // passes the array's name to a kernel (on the host it is a stand-in, not a
 // device address): it looks the address up once per device and passes that.
-static __device__ __align__(256) float scratch[SEPATTN_BWD_NOALLOC_MAX_ROWS];
+static __device__ __align__(256) float scratch[SEPATTN_BWD_NOALLOC_MAX_ROWS + SEPATTN_BWD_QUEUE_BYTES / 4];
 
 namespace {
 constexpr int kMaxDevices = 64;
@@ -671,8 +717,9 @@ int sepattn_launch_bwd_noalloc(const sepattn_shape* s, int dtype, const sepattn_
                                float scale, void* dq, void* dk, void* dv, hipStream_t st) {
   float* ws = nullptr;
   SEPATTN_TRY(scratch_address(&ws));
-  // D is written for every row by the dQ kernel before the dK/dV kernel
-  // reads it, so nothing needs clearing between calls
+  // D is written for every row, and the counters are cleared, by the dQ
+  // kernel before the dK/dV kernel reads them, so nothing needs clearing
+  // between calls
   return sepattn_launch_bwd(s, dtype, m, q, k, v, o, lse, dout, scale, dq, dk, dv, ws, st);
 }
 
@@ -684,6 +731,7 @@ int sepattn_launch_bwd(const sepattn_shape* s, int dtype, const sepattn_mask* m,
   p.q = (const bf16*)q; p.k = (const bf16*)k; p.v = (const bf16*)v; p.o = (const bf16*)o;
   p.dout = (const bf16*)dout; p.lse = lse;
   p.dq = (bf16*)dq; p.dk = (bf16*)dk; p.dv = (bf16*)dv; p.dsum = dsum;
+  p.queue = (uint32_t*)((char*)dsum + sepattn_bwd_d_bytes(s));
   for (int i = 0; i < 3; ++i) {
     p.sq[i] = s->q_stride[i]; p.sk[i] = s->k_stride[i]; p.sv[i] = s->v_stride[i]; p.so[i] = s->o_stride[i];
   }

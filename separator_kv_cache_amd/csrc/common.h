@@ -15,6 +15,13 @@ int sepattn_hip_check(hipError_t e, const char* what);
 // Returns SEPATTN_OK if the current device is gfx950, else an error.
 int sepattn_check_device();
 
+// The backward's workspace: D, fp32 [B, Hq, L], rounded up to 256 bytes, then
+// the dK/dV kernel's tile counters.
+constexpr size_t SEPATTN_BWD_QUEUE_BYTES = 1024;
+inline size_t sepattn_bwd_d_bytes(const sepattn_shape* s) {
+  return ((size_t)s->B * s->Hq * s->L * 4 + 255) / 256 * 256;
+}
+
 #define SEPATTN_TRY(x)          \
   do {                          \
     int _rc = (x);              \
